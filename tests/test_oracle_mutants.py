@@ -1,0 +1,120 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case swaps one oracle function for a plausible wrong variant (a
+dropped term, a wrong rounding rule, a flipped orientation, a transposed
+operand) and checks that at least one pin then fails.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.svdquant as osq
+from tests import test_oracle_quant as tq
+from tests import test_oracle_split as ts
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(osq, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _expect_fail(*pins):
+    failed = 0
+    for pin, args in pins:
+        try:
+            pin(*args)
+        except AssertionError:
+            failed += 1
+    assert failed > 0, "planted mistake went unnoticed"
+
+
+def test_mutant_int4_round_half_away(monkeypatch):
+    orig = osq.quant_int4_g64
+
+    def bad(v):
+        q, s = orig(v)
+        s32 = s.view(np.float16).astype(np.float32)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            r = (np.asarray(v, np.float32) / s32[..., None]).astype(np.float32)
+        qa = np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -7, 7)
+        qa = np.where(s32[..., None] == 0, 0, np.nan_to_num(qa))
+        return qa.astype(np.int8), s
+    _patch(monkeypatch, "quant_int4_g64", bad)
+    _expect_fail((tq.test_int4_worked_example, ()), (tq.test_int4_against_scalar_restatement, (1.0,)))
+
+
+def test_mutant_mxfp4_floor_scale(monkeypatch):
+    orig = osq.quant_mxfp4_g32
+
+    def bad(v):
+        v = np.asarray(v, np.float32)
+        m = np.max(np.abs(v), -1).astype(np.float32)
+        t = (m / np.float32(6)).astype(np.float32)
+        e = ((t.view(np.uint32) >> 23) & 0xFF).astype(np.int64)   # floor exponent, no round-up
+        u = np.ldexp(v, (127 - e)[..., None].astype(np.int32)).astype(np.float32)
+        idx = osq._e2m1_nearest_even(np.abs(u))
+        return (idx | (np.signbit(v).astype(np.uint8) << 3)).astype(np.uint8), e.astype(np.uint8)
+    _patch(monkeypatch, "quant_mxfp4_g32", bad)
+    _expect_fail((tq.test_mxfp4_worked_examples, ("mxfp4_g32_scale_up.txt",)),
+                 (tq.test_mxfp4_scale_is_smallest_power_of_two_covering, ()))
+
+
+def test_mutant_residual_drops_lambda(monkeypatch):
+    def bad(W, lam, L1x, L2q):
+        W = np.asarray(W, np.float64); lam64 = np.asarray(lam, np.float64)
+        s = np.asarray(L1x, np.float64) @ np.asarray(L2q, np.float64)
+        return (lam64[:, None] * W - s).astype(np.float32)
+    _patch(monkeypatch, "residual", bad)
+    _expect_fail((ts.test_residual_reconstructs_to_fp32_rounding, ()))
+
+
+def test_mutant_svd_drops_sigma(monkeypatch):
+    def bad(W_hat, r):
+        U, S, Vt = np.linalg.svd(W_hat, full_matrices=False)
+        return U[:, :r].copy(), Vt[:r].copy(), S
+    _patch(monkeypatch, "truncated_svd", bad)
+    _expect_fail((ts.test_eckart_young_mirsky, ((128, 96),)))
+
+
+def test_mutant_smoothing_inverted(monkeypatch):
+    orig = osq.smoothing_factors
+
+    def bad(a, w):
+        lam, inv = orig(a, w)
+        return inv, lam
+    _patch(monkeypatch, "smoothing_factors", bad)
+    _expect_fail((ts.test_smoothing_balances_channel_maxima, ()))
+
+
+def test_mutant_forward_drops_up_projection(monkeypatch):
+    def bad(Y_main, T, L2q, bias, gelu):
+        Y = np.asarray(Y_main, np.float64)
+        if bias is not None:
+            Y = Y + np.asarray(bias, np.float64)[None, :]
+        return Y
+    _patch(monkeypatch, "output_epilogue_f64", bad)
+    _expect_fail((ts.test_brute_force_tiny, (oracle.INT4, 64, oracle.F16)))
+
+
+def test_mutant_mx_scales_wrong_axis(monkeypatch):
+    orig = osq.dequant_weight
+
+    def bad(q, s, fmt):
+        if fmt != oracle.MXFP4:
+            return orig(q, s, fmt)
+        s2 = np.ascontiguousarray(s[::-1])       # group scales applied to the wrong K-groups
+        return orig(q, s2, fmt)
+    _patch(monkeypatch, "dequant_weight", bad)
+    _expect_fail((ts.test_brute_force_tiny, (oracle.MXFP4, 128, oracle.BF16)))
+
+
+def test_mutant_int4_partial_sign(monkeypatch):
+    orig = osq.int4_group_partials
+
+    def bad(qx, qw):
+        P = orig(qx, qw)
+        P[-1] = -P[-1]                            # wrong sign on one group
+        return P
+    _patch(monkeypatch, "int4_group_partials", bad)
+    _expect_fail((ts.test_brute_force_tiny, (oracle.INT4, 128, oracle.F16)),
+                 (ts.test_rank0_unit_lambda_is_naive_w4a4, ()))
