@@ -1,0 +1,146 @@
+// svdq_layout.h -- byte layout of the packed layer blob and of the forward
+// workspace.  Shared by the host pack and the device launch code of the
+// library (not by any checker).
+//
+// Every 4-bit operand is stored as matrix-core fragments: for a 16-wide
+// tile of rows (output columns n for the weight, tokens m for activations)
+// and a 128-deep step of K, 64 lanes x 16 bytes.  Lane l covers row
+// (l % 16) and the K quarter q = l / 16 of the step:
+//   MXFP4: the 16 bytes are the 32 E2M1 codes of k in [32q, 32q+32) of the
+//          step (element 2i in the low nibble of byte i) -- one e8m0 block.
+//   INT4:  bytes [0, 8)  hold k in [16q, 16q+16)      (first 64-group),
+//          bytes [8, 16) hold k in [64+16q, 64+16q+16) (second 64-group).
+// A wave then loads a whole fragment with one 16-byte load per lane.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace svdq {
+
+constexpr int KSTEP = 128;         // K covered by one fragment step
+constexpr int FRAG_BYTES = 1024;   // 64 lanes x 16 bytes
+constexpr int M_PAD = 256;         // workspace rows are padded to this
+constexpr int HDR_BYTES = 256;
+constexpr uint32_t BLOB_MAGIC = 0x51445653u;   // "SVDQ"
+constexpr uint32_t BLOB_VERSION = 1u;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline int group_size(int fmt) { return fmt == 0 ? 64 : 32; }
+
+// Header at the start of every blob (all later offsets are relative to the blob).
+struct BlobHeader {
+  uint32_t magic, version;
+  int64_t K, N;
+  int32_t rank, rank_active, rank_capacity, rank_slots, fmt, dtype, has_bias, pad0;
+  uint64_t off_invlam, off_lam, off_l1x, off_l2, off_wq, off_sw, off_bias, total;
+};
+static_assert(sizeof(BlobHeader) <= HDR_BYTES, "header too large");
+
+struct BlobOffsets {
+  size_t invlam, lam, l1x, l2, wq, sw, bias, total;
+};
+
+// bytes of the weight scales
+inline size_t weight_scale_bytes(int64_t K, int64_t N, int fmt) {
+  if (fmt == 1) return size_t(N / 16) * size_t(ceil_div(K, 512)) * 64 * 4;   // MX: 4 steps per dword
+  return size_t(N / 16) * size_t(K / KSTEP) * 64;                           // INT4: 2 groups x 16 rows x fp16
+}
+
+inline BlobOffsets blob_offsets(int64_t K, int64_t N, int slots, int fmt) {
+  BlobOffsets o;
+  size_t p = HDR_BYTES;
+  o.invlam = p; p = align256(p + size_t(K) * 4);
+  o.lam = p;    p = align256(p + size_t(K) * 4);
+  o.l1x = p;    p = align256(p + size_t(K) * slots * 2);
+  o.l2 = p;     p = align256(p + size_t(slots) * N * 2);
+  o.wq = p;     p = align256(p + size_t(K) * N / 2);
+  o.sw = p;     p = align256(p + weight_scale_bytes(K, N, fmt));
+  o.bias = p;   p = align256(p + size_t(N) * 4);
+  o.total = p;
+  return o;
+}
+
+struct WsOffsets {
+  int64_t Mp;
+  size_t xq, sx, t, total;
+};
+
+inline size_t act_scale_bytes(int64_t Mp, int64_t K, int fmt) {
+  if (fmt == 1) return size_t(Mp / 16) * size_t(ceil_div(K, 512)) * 64 * 4;
+  return size_t(Mp / 16) * size_t(K / KSTEP) * 64;
+}
+
+inline WsOffsets ws_offsets(int64_t M, int64_t K, int slots, int fmt) {
+  WsOffsets w;
+  w.Mp = round_up(M > 0 ? M : 1, M_PAD);
+  size_t p = 0;
+  w.xq = p; p = align256(p + size_t(w.Mp) * K / 2);
+  w.sx = p; p = align256(p + act_scale_bytes(w.Mp, K, fmt));
+  w.t = p;  p = align256(p + size_t(w.Mp) * slots * 2);
+  w.total = p;
+  return w;
+}
+
+// ---- element -> position maps (used by the host pack and the exporters) ----
+
+// 4-bit code of (row r, k) in a fragment array with K columns: byte offset
+// and nibble (0 = low) within it.
+inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int* nib) {
+  int64_t t = r / 16, s = k / KSTEP, kk = k % KSTEP;
+  int64_t lane, b;
+  if (fmt == 1) {
+    int64_t q = kk / 32, c = kk % 32;
+    lane = (r % 16) + 16 * q;
+    b = c / 2;
+    *nib = int(c % 2);
+  } else {
+    int64_t g = kk / 64, w = kk % 64, q = w / 16, c = w % 16;
+    lane = (r % 16) + 16 * q;
+    b = 8 * g + c / 2;
+    *nib = int(c % 2);
+  }
+  *byte = size_t(((t * (K / KSTEP) + s) * 64 + lane) * 16 + b);
+}
+
+// MX e8m0 scale of (row r, 32-block b): byte offset.
+inline size_t mx_scale_pos(int64_t r, int64_t b, int64_t K) {
+  int64_t t = r / 16, s = b / 4, q = b % 4;
+  int64_t lane = (r % 16) + 16 * q;
+  int64_t quads = ceil_div(K, 512);
+  return size_t(((t * quads + s / 4) * 64 + lane) * 4 + (s % 4));
+}
+
+// INT4 fp16 scale of weight (column n, 64-group G): element (uint16) offset.
+// Per (16-column tile, step): [q = (n%16)/4][group in step][n % 4].
+inline size_t int4_wscale_pos(int64_t n, int64_t G, int64_t K) {
+  int64_t t = n / 16, s = G / 2, g = G % 2, q = (n % 16) / 4, i = n % 4;
+  return size_t((((t * (K / KSTEP) + s) * 4 + q) * 2 + g) * 4 + i);
+}
+
+// INT4 fp16 scale of activation (token m, 64-group G): element offset.
+// Per (16-token tile, step): [m % 16][group in step].
+inline size_t int4_xscale_pos(int64_t m, int64_t G, int64_t K) {
+  int64_t t = m / 16, s = G / 2, g = G % 2;
+  return size_t(((t * (K / KSTEP) + s) * 16 + (m % 16)) * 2 + g);
+}
+
+// 16-bit low-rank operand of the GEMM epilogue: (row r, rank j), rows are
+// n for L2 and m for T.  Per (16-row tile, 32-rank chunk): 64 lanes x 8.
+inline size_t lr_pos(int64_t r, int64_t j, int slots) {
+  int64_t t = r / 16, c = j / 32, jj = j % 32, q = jj / 8, e = jj % 8;
+  int64_t lane = (r % 16) + 16 * q;
+  return size_t(((t * (slots / 32) + c) * 64 + lane) * 8 + e);
+}
+
+// 16-bit L1x as the activation kernel reads it: (k, rank j).
+// Per (128-step, 16-rank tile, 32-K sub-step j'): 64 lanes x 8; lane covers
+// rank (j % 16) and k in [32q + 8j', 32q + 8j' + 8) of the step.
+inline size_t l1x_pos(int64_t k, int64_t j, int slots) {
+  int64_t s = k / KSTEP, kk = k % KSTEP, q = kk / 32, w = kk % 32, jp = w / 8, e = w % 8, jt = j / 16;
+  int64_t lane = (j % 16) + 16 * q;
+  return size_t((((s * (slots / 16) + jt) * 4 + jp) * 64 + lane) * 8 + e);
+}
+
+}  // namespace svdq

@@ -1,0 +1,202 @@
+/*
+ * svdq.h -- C ABI of the SVDQuant linear layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer computes, for activations X (M x K) and a weight W (K x N),
+ *
+ *     Y = (X diag(lambda)^-1) L1 L2  +  Q(X diag(lambda)^-1) Q(R)  (+ bias)
+ *
+ * SVDQuant paper ("SVDQuant: Absorbing Outliers by Low-Rank Components for
+ * 4-Bit Diffusion Models", translated article on developer.volcengine.com):
+ *   - smoothing by per-channel factors lambda            §4.2, Fig. 4
+ *   - rank-r SVD split W_hat = L1 L2 + R                 §4.2, Eq. 5, Fig. 5
+ *   - symmetric group quantizer Q, INT4 / FP4            §3; §5.1 impl. details
+ *   - down-projection fused with the activation quantizer,
+ *     up-projection fused with the 4-bit product         §4.3, Fig. 6b
+ *   - LoRA concatenated into the low-rank branch         §5.2 (LoRA), §1
+ *
+ * Conventions for every entry point:
+ *   - Every call returns an svdq_status; nothing throws or aborts across
+ *     the ABI.  Argument and shape errors are reported synchronously before
+ *     anything is launched.
+ *   - All device memory (packed blob, X, Y, workspace) is allocated and owned
+ *     by the caller.  The library never allocates device memory.
+ *   - Row-major storage.  X is M x K with row stride ldx elements, Y is
+ *     M x N with row stride ldy elements, both in the layer's 16-bit dtype.
+ *   - Host buffers passed to synchronous calls may be freed on return.
+ *   - Forward calls are asynchronous on the caller's stream; forwards on
+ *     different streams may run concurrently.  Attaching/detaching a LoRA
+ *     must not race with forwards of the same layer.
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SVDQ_OK = 0,
+  SVDQ_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, negative size, bad rank */
+  SVDQ_ERR_SHAPE = 2,        /* K not a multiple of 128, N of 128, strides too small */
+  SVDQ_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement */
+  SVDQ_ERR_CAPACITY = 4,     /* buffer too small, LoRA rank beyond the capacity */
+  SVDQ_ERR_NUMERIC = 5,      /* non-finite weights or calibration maxima */
+  SVDQ_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
+} svdq_status;
+
+typedef enum {
+  SVDQ_FMT_INT4_G64 = 0,     /* signed INT4 codes in [-7, 7], group 64 along K, fp16 scales */
+  SVDQ_FMT_MXFP4_G32 = 1     /* E2M1 codes, group 32 along K, e8m0 (power-of-two) scales */
+} svdq_format;
+
+typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+
+enum {
+  SVDQ_FLAG_GELU = 1u        /* apply x * Phi(x) (erf GELU) to Y before rounding */
+};
+
+#define SVDQ_MAX_RANK_CAPACITY 128
+
+/* Descriptor of one packed layer (plain data, caller-owned).  It points into
+ * the caller's blob; all offsets are bytes from `blob`.  The blob holds no
+ * absolute pointers, so copying its bytes moves the layer (save/restore). */
+typedef struct {
+  int64_t K, N;
+  int32_t rank;            /* SVD rank r of the split */
+  int32_t rank_active;     /* r + rank of the attached LoRA */
+  int32_t rank_capacity;   /* factor slots reserved at pack time (>= rank) */
+  int32_t rank_slots;      /* rank_capacity rounded up to a multiple of 32 */
+  int32_t fmt;             /* svdq_format */
+  int32_t dtype;           /* svdq_dtype */
+  int32_t has_bias;
+  int32_t blob_on_device;  /* 1: blob is device memory, 0: host memory */
+  void* blob;
+  size_t blob_bytes;
+  size_t off_invlam, off_lam, off_l1x, off_l2, off_wq, off_sw, off_bias;
+} svdq_layer;
+
+const char* svdq_status_string(svdq_status s);
+
+/* ---------------------------------------------------------------- pack --- */
+
+/* Bytes of the packed blob for a K x N layer with `rank_capacity` factor
+ * slots.  Layout: header, 1/lambda and lambda (fp32 [K]), L1x (16-bit,
+ * K x slots, tiled for the activation kernel), L2 (16-bit, slots x N, tiled
+ * for the GEMM epilogue), residual codes (4-bit, K x N, tiled as matrix-core
+ * fragments), group scales, bias (fp32 [N]). */
+svdq_status svdq_packed_size(int64_t K, int64_t N, int rank_capacity, svdq_format fmt,
+                             svdq_dtype dtype, size_t* bytes);
+
+/* Offline post-training quantization of one linear layer (SVDQuant §4.2):
+ *   lambda_j = sqrt(act_absmax[j] / max_n |W[j,n]|) (fp32; 1 for a zero
+ *     channel or when act_absmax is NULL),
+ *   W_hat = diag(lambda) W, truncated SVD W_hat ~ L1 L2 with L1 = U_r S_r,
+ *   L1x = 16-bit(diag(1/lambda) L1), L2 = 16-bit(V_r^T),
+ *   R = fp32(W_hat - diag(lambda) L1x L2), quantized per output column in
+ *   K-groups (INT4 g64 / MXFP4 g32), all tiled for the GEMM.
+ * W_host: K x N, 16-bit `dtype`, row stride ldw.  act_absmax_host: [K] fp32
+ * per-channel calibration maxima of |X| or NULL.  bias_host: [N] 16-bit or
+ * NULL.  0 <= rank <= min(K, N, rank_capacity), rank_capacity <=
+ * SVDQ_MAX_RANK_CAPACITY.  Requires K % 128 == 0 and N % 128 == 0.
+ * svdq_pack_weights writes the blob to device memory blob_dev (>=
+ * svdq_packed_size bytes) and returns after the copy finished on `stream`;
+ * svdq_pack_weights_host writes it to host memory.  `out` receives the
+ * descriptor.  Synchronous. */
+svdq_status svdq_pack_weights(const void* W_host, int64_t K, int64_t N, int64_t ldw, svdq_dtype dtype,
+                              const float* act_absmax_host, int rank, int rank_capacity, svdq_format fmt,
+                              const void* bias_host, void* blob_dev, size_t blob_bytes, hipStream_t stream,
+                              svdq_layer* out);
+svdq_status svdq_pack_weights_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, svdq_dtype dtype,
+                                   const float* act_absmax_host, int rank, int rank_capacity, svdq_format fmt,
+                                   const void* bias_host, void* blob_host, size_t blob_bytes, svdq_layer* out);
+
+/* Copy a packed layer's blob (host or device) to another buffer (host or
+ * device) and describe the copy in `out` (restore / upload).  dst_on_device
+ * selects the destination kind.  Synchronous on `stream`. */
+svdq_status svdq_layer_copy(const svdq_layer* src, void* dst, size_t dst_bytes, int dst_on_device,
+                            hipStream_t stream, svdq_layer* out);
+
+/* Concatenate a LoRA (A: K x rL, B: rL x N, 16-bit host matrices, row-major)
+ * into the low-rank branch: L1x[:, rank:rank+rL] = A, L2[rank:rank+rL, :] =
+ * 16-bit(alpha * B).  The residual and its codes are untouched (no
+ * re-quantization, SVDQuant §5.2).  Replaces any LoRA attached before.
+ * Error SVDQ_ERR_CAPACITY if rank + rL > rank_capacity.  Synchronous. */
+svdq_status svdq_attach_lora(svdq_layer* layer, const void* A_host, const void* B_host, int rL,
+                             float alpha, hipStream_t stream);
+/* Zero the LoRA slots and set rank_active = rank.  Synchronous. */
+svdq_status svdq_detach_lora(svdq_layer* layer, hipStream_t stream);
+
+/* ------------------------------------------------------------- forward --- */
+
+/* Bytes of device workspace a forward of M tokens needs (4-bit activation
+ * codes and scales, and the 16-bit down-projection T = X L1x). */
+svdq_status svdq_workspace_size(const svdq_layer* layer, int64_t M, size_t* bytes);
+
+/* Y = X_hat L1x L2 + Q(X_hat) Q(R) + bias [-> GELU], rounded to the layer's
+ * dtype (SVDQuant §4.2 Eq. 5, fused as in §4.3).  Two kernels on `stream`:
+ * the activation kernel (smoothing, group quantization, down-projection,
+ * one pass over X) and the 4-bit GEMM with the up-projection, bias and
+ * optional GELU in its epilogue.  X_dev: M x K (ldx >= K, ldx % 8 == 0,
+ * 16-byte aligned); Y_dev: M x N (ldy >= N, ldy % 4 == 0, 8-byte aligned);
+ * ws_dev: >= svdq_workspace_size bytes, 256-byte aligned.  M >= 0 (M == 0
+ * is a no-op).  Asynchronous. */
+svdq_status svdq_linear_forward(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
+                                void* Y_dev, int64_t ldy, void* ws_dev, size_t ws_bytes, unsigned flags,
+                                hipStream_t stream);
+
+/* The two stages of svdq_linear_forward, callable on their own (the second
+ * reads what the first wrote into ws_dev).  Asynchronous. */
+svdq_status svdq_quantize_activations(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
+                                      void* ws_dev, size_t ws_bytes, hipStream_t stream);
+svdq_status svdq_gemm_forward(const svdq_layer* layer, int64_t M, void* Y_dev, int64_t ldy,
+                              const void* ws_dev, size_t ws_bytes, unsigned flags, hipStream_t stream);
+
+/* Calibration statistic for smoothing (SVDQuant §4.2): absmax_dev[k] =
+ * max(absmax_dev[k], max_m |X[m,k]|), fp32, exact.  Initialise absmax_dev to
+ * zero before the first batch.  Asynchronous. */
+svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int64_t ldx, svdq_dtype dtype,
+                                   float* absmax_dev, hipStream_t stream);
+
+/* --------------------------------------------------------- inspection --- */
+
+/* Canonical (untiled) copies of a packed layer, written to host buffers;
+ * any output pointer may be NULL.  lam, invlam: [K] fp32.  l1x: K x
+ * rank_active 16-bit.  l2: rank_active x N 16-bit.  codes: K x N bytes
+ * (INT4: int8 value in [-7, 7]; MXFP4: E2M1 code 0..15).  scales: (K/G) x N
+ * (INT4: fp16 bits as uint16; MXFP4: e8m0 bytes).  bias: [N] fp32.
+ * Synchronous (copies the blob from the device when it lives there). */
+svdq_status svdq_layer_export(const svdq_layer* layer, float* lam, float* invlam, void* l1x, void* l2,
+                              void* codes, void* scales, float* bias, hipStream_t stream);
+
+/* Canonical copies of what svdq_quantize_activations wrote for M tokens:
+ * codes M x K bytes (as above), scales M x (K/G), t: M x rank_active
+ * 16-bit (the rounded down-projection).  Synchronous. */
+svdq_status svdq_workspace_export(const svdq_layer* layer, const void* ws_dev, size_t ws_bytes, int64_t M,
+                                  void* codes, void* scales, void* t, hipStream_t stream);
+
+/* The fp64 factors of the truncated SVD the pack uses, before any 16-bit
+ * rounding: L1 (K x rank) = U_r S_r, L2 (rank x N) = V_r^T, sigma[rank] the
+ * top singular values, and lambda [K].  Host only, synchronous. */
+svdq_status svdq_svd_factors(const void* W_host, int64_t K, int64_t N, int64_t ldw, svdq_dtype dtype,
+                             const float* act_absmax_host, int rank, double* L1, double* L2, double* sigma,
+                             float* lam);
+
+/* INT4 layers only: the per-group integer products P_g[m,n] = sum over the
+ * 64 k of group g of code_x[m,k] code_w[k,n], as the GEMM's integer matrix
+ * instructions produce them, for the window m in [m0, m0+nm), n in
+ * [n0, n0+nn), g in [g0, g0+ng).  out_dev: int32 [ng][nm][nn] device
+ * buffer.  Reads the codes svdq_quantize_activations left in ws_dev.
+ * Requires m0 % 16 == 0, n0 % 16 == 0, nm % 16 == 0, nn % 16 == 0.
+ * Asynchronous. */
+svdq_status svdq_int4_group_partials(const svdq_layer* layer, const void* ws_dev, size_t ws_bytes, int64_t M,
+                                     int64_t m0, int64_t nm, int64_t n0, int64_t nn, int64_t g0, int64_t ng,
+                                     int32_t* out_dev, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SVDQ_H */
