@@ -1,0 +1,247 @@
+"""Benchmark of the SVDQuant linear (fused W4A4 + low-rank) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--fmt mxfp4|int4] [--workload fc1|...]
+
+A step is one forward of the layer -- activation kernel (smoothing, 4-bit
+group quantization, low-rank down-projection) then the 4-bit GEMM with the
+up-projection, bias and rounding in its epilogue -- over one batch of
+synthetic tokens already resident in HBM.  The pack (smoothing factors, SVD,
+residual quantization) is offline and not timed.
+
+Default workload: the FLUX.1-shaped MLP fc1 linear at 1024^2 (4608 tokens x
+3072 -> 12288), bf16 activations, MXFP4 group 32 with e8m0 scales, rank 32.
+Metric: effective TOPS = 2 M K N / t (the low-rank FLOPs are not counted).
+
+Prints one JSON line.  The CPU baseline is the CPU oracle's float32 forward
+timed on a bounded sample of the same layer, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective TOPS of fused W4A4+low-rank linear (FLUX fc1 shape), % of MFMA peak"
+PEAK_TFLOPS = {"mxfp4_g32": 10100.0, "int4_g64": 5000.0}     # MI355X dense MFMA: fp4, int8
+HBM_PEAK_GBS = 8000.0
+
+WORKLOADS = {
+    # name: (M, K, N, dtype)
+    "fc1": (4608, 3072, 12288, "bf16"),
+    "fc2": (4608, 12288, 3072, "bf16"),
+    "qkv": (4608, 3072, 9216, "bf16"),
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "int4"])
+    ap.add_argument("--workload", default="fc1", choices=sorted(WORKLOADS))
+    ap.add_argument("--rank", type=int, default=32)
+    ap.add_argument("--rotate", type=int, default=4, help="distinct X/Y/weight buffer sets cycled per step")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--kernel-iters", type=int, default=50)
+    return ap.parse_args()
+
+
+def k1_bytes(M, K, r, fmt):
+    G = 64 if fmt == "int4_g64" else 32
+    sb = 2 if fmt == "int4_g64" else 1
+    return 2 * M * K + M * K // 2 + (M * K // G) * sb + 2 * M * r + 2 * K * r + 4 * K
+
+
+def k2_bytes(M, K, N, r, fmt):
+    G = 64 if fmt == "int4_g64" else 32
+    sb = 2 if fmt == "int4_g64" else 1
+    return (M * K // 2 + (M * K // G) * sb + K * N // 2 + (K * N // G) * sb + 2 * M * r + 2 * r * N
+            + 4 * N + 2 * M * N)
+
+
+def cpu_baseline(spec, d, lin_export, fmt_name, rank):
+    """The oracle's float32 forward on a bounded sample of the layer."""
+    import threadpoolctl  # noqa: F401  (reports the BLAS threads)
+    from threadpoolctl import threadpool_info
+    import oracle as o
+    rows, cols = 512, 2048
+    W = np.ascontiguousarray(d["W"][:, :cols])
+    L2q = np.ascontiguousarray(lin_export["L2q"][:, :cols])
+    pf = o.pack_from_factors(W, spec.dtype, lin_export["lam"], lin_export["L1x"][:, :rank], L2q[:rank], fmt_name)
+    layer = {"dtype": spec.dtype, "fmt": fmt_name, "lam": lin_export["lam"], "invlam": lin_export["invlam"],
+             "L1x": lin_export["L1x"], "L2q": L2q, "qw": pf["qw"], "sw": pf["sw"],
+             "bias": None if d["bias"] is None else d["bias"][:cols]}
+    Xs = np.ascontiguousarray(d["X"][:rows])
+    o.forward_fp32_timed(layer, Xs)          # warm (dequantizes the weight once)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        o.forward_fp32_timed(layer, Xs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el > 8.0 or reps >= 20:
+            break
+    t = el / reps
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": 2.0 * rows * spec.K * cols / t / 1e12, "unit": "TOPS", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows} of {spec.M} tokens x {cols} of {spec.N} output columns, oracle float32 path "
+                      f"(activation quantization, dequantized sgemm, up-projection, bias), {reps} reps, "
+                      f"{t * 1e3:.1f} ms each; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
+              f"is a design note, not a run.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from diffusion_smooth_group_amd import svdq as S
+    from diffusion_smooth_group_amd import workloads as wl
+
+    fmt_name = "mxfp4_g32" if args.fmt == "mxfp4" else "int4_g64"
+    fmt = S.FMT_MXFP4_G32 if args.fmt == "mxfp4" else S.FMT_INT4_G64
+    M, K, N, dts = WORKLOADS[args.workload]
+    dt = S.BF16 if dts == "bf16" else S.F16
+    if args.workload == "fc1":
+        spec = wl.config_shapes(3)[0]
+    elif args.workload == "fc2":
+        spec = wl.config_shapes(3)[1]
+    else:
+        spec = wl.config_shapes(2)[0]
+    assert (spec.M, spec.K, spec.N) == (M, K, N)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    d = wl.generate(spec)
+    Xd0 = S.bits_to_device(d["X"], dt, dev)
+    absmax = S.activation_absmax(Xd0, dt)
+    torch.cuda.synchronize()
+    lin = S.SVDQLinear.pack(d["W"], dt, absmax.cpu().numpy(), args.rank, fmt, d["bias"], rank_capacity=args.rank)
+    t_pack = time.time() - t0
+    torch.cuda.synchronize()
+
+    # rotating buffer sets so the 256 MB last-level cache cannot hold a step's working set
+    nrot = max(1, args.rotate)
+    Xs = [Xd0] + [Xd0.clone() for _ in range(nrot - 1)]
+    Ys = [torch.empty((M, N), dtype=Xd0.dtype, device=dev) for _ in range(nrot)]
+    layers = [lin.layer]
+    blobs = [lin.blob]
+    for _ in range(nrot - 1):
+        b = torch.empty_like(lin.blob)
+        layers.append(S.layer_copy(lin.layer, S._t_ptr(b), b.numel(), True))
+        blobs.append(b)
+    ws_bytes = S.workspace_size(lin.layer, M)
+    wss = [torch.empty(ws_bytes, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+    lib = S.lib_handle()
+    import ctypes as C
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+
+    def fwd(i):
+        j = i % nrot
+        rc = lib.svdq_linear_forward(C.byref(layers[j]), S._t_ptr(Xs[j]), M, K, S._t_ptr(Ys[j]), N,
+                                     S._t_ptr(wss[j]), ws_bytes, 0, sh)
+        if rc != 0:
+            raise S.SvdqError("svdq_linear_forward", rc)
+
+    def k1(i):
+        j = i % nrot
+        rc = lib.svdq_quantize_activations(C.byref(layers[j]), S._t_ptr(Xs[j]), M, K, S._t_ptr(wss[j]), ws_bytes, sh)
+        if rc != 0:
+            raise S.SvdqError("svdq_quantize_activations", rc)
+
+    def k2(i):
+        j = i % nrot
+        rc = lib.svdq_gemm_forward(C.byref(layers[j]), M, S._t_ptr(Ys[j]), N, S._t_ptr(wss[j]), ws_bytes, 0, sh)
+        if rc != 0:
+            raise S.SvdqError("svdq_gemm_forward", rc)
+
+    for i in range(args.warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` forwards
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    tw0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        fwd(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    # ---- per-kernel launch durations (HIP events on the launch stream)
+    def per_launch(fn, n):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i in range(n):
+            evs[i][0].record(stream)
+            fn(i)
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        ts = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3   # us
+        return float(np.mean(ts)), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+
+    for i in range(nrot):       # workspaces hold this step's activations for k2-only timing
+        k1(i)
+    torch.cuda.synchronize()
+    k1_stats = per_launch(k1, args.kernel_iters)
+    k2_stats = per_launch(k2, args.kernel_iters)
+
+    flops = 2.0 * M * K * N
+    tops = flops / (ms_step * 1e-3) / 1e12
+    k2_tflops = flops / (k2_stats[0] * 1e-6) / 1e12
+    k1_gbs = k1_bytes(M, K, args.rank, fmt_name) / (k1_stats[0] * 1e-6) / 1e9
+    peak = PEAK_TFLOPS[fmt_name]
+    out = {
+        "metric": METRIC,
+        "value": round(tops, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4" if fmt == S.FMT_MXFP4_G32 else "int4",
+        "data": "synthetic",
+        "config": {"workload": f"flux_{args.workload}_{M}x{K}x{N}", "M": M, "K": K, "N": N, "rank": args.rank,
+                   "format": fmt_name, "activation_dtype": dts, "parallelism": "single GPU",
+                   "rotating_buffer_sets": nrot},
+        "pct_of_peak": round(100.0 * tops / peak, 2),
+        "roofline": {"bound": "mfma", "kernel": "k2_gemm", "achieved": round(k2_tflops, 1), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": k2_bytes(M, K, N, args.rank, fmt_name)},
+        "k1_roofline": {"bound": "hbm", "kernel": "k1_act", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes_per_launch": k1_bytes(M, K, args.rank, fmt_name)},
+        "kernel_us": {"k1_act": {"mean": round(k1_stats[0], 2), "median": round(k1_stats[1], 2),
+                                 "p10": round(k1_stats[2], 2), "p90": round(k1_stats[3], 2)},
+                      "k2_gemm": {"mean": round(k2_stats[0], 2), "median": round(k2_stats[1], 2),
+                                  "p10": round(k2_stats[2], 2), "p90": round(k2_stats[3], 2)}},
+        "gemm_only_tops": round(k2_tflops, 2),
+        "timed_wall_s": round(wall, 4),
+        "pack_s": round(t_pack, 2),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(spec, d, lin.export(), fmt_name, args.rank)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
