@@ -25,7 +25,7 @@
 
 #include <cstdint>
 
-#include "../../include/svdq.h"
+#include "svdq.h"
 #include "svdq_layout.h"
 
 namespace svdq {
@@ -100,7 +100,6 @@ __global__ __launch_bounds__(256) void k1_act(K1Params p) {
   const int64_t row = int64_t(mt) * 16 + m;
   const bool valid = row < p.M;
   const int nsteps = int(p.K / KSTEP);
-  const int quads = int((p.K + 511) / 512);
   const uint16_t* xrow = p.X + (valid ? row : 0) * p.ldx;
 
   f32x4 tacc[MAXJT];
@@ -167,7 +166,8 @@ __global__ __launch_bounds__(256) void k1_act(K1Params p) {
         d[i >> 3] |= c << (4 * (i & 7));
       }
       *reinterpret_cast<u32x4*>(frag + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
-      p.sx[((size_t(mt) * quads + (s >> 2)) * 64 + lane) * 4 + (s & 3)] = (uint8_t)e;
+      // byte (mt % 4) of the dword of tile group mt / 4 (selected by op_sel in the GEMM)
+      p.sx[((size_t(mt >> 2) * nsteps + s) * 64 + lane) * 4 + (mt & 3)] = (uint8_t)e;
     }
 
     // down-projection T^T += L1x^T X^T on the raw 16-bit inputs
@@ -228,10 +228,10 @@ __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
 
 __device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
 
-// One workgroup = 128 output columns x 128 tokens; 4 waves in a 2 x 2 grid,
-// each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).
-template <int FMT, int DT, bool GELU>
-__global__ __launch_bounds__(256) void k2_gemm(K2Params p) {
+// INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
+// 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).
+template <int DT, bool GELU>
+__global__ __launch_bounds__(256) void k2_int4(K2Params p) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
@@ -239,7 +239,6 @@ __global__ __launch_bounds__(256) void k2_gemm(K2Params p) {
   const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
   const int64_t nt0 = n0 / 16, mt0 = m0 / 16;
   const int nsteps = int(p.K / KSTEP);
-  const int quads = int((p.K + 511) / 512);
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -256,25 +255,7 @@ __global__ __launch_bounds__(256) void k2_gemm(K2Params p) {
     for (int i = 0; i < 4; ++i) a[i] = wq[((nt0 + i) * nsteps + s) * 64 + lane];
 #pragma unroll
     for (int j = 0; j < 4; ++j) b[j] = xq[((mt0 + j) * nsteps + s) * 64 + lane];
-    if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
-      const unsigned* swd = reinterpret_cast<const unsigned*>(p.sw);
-      const unsigned* sxd = reinterpret_cast<const unsigned*>(p.sx);
-      const int shift = 8 * (s & 3);
-      int sa[4], sb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sa[i] = int(swd[((nt0 + i) * quads + (s >> 2)) * 64 + lane] >> shift);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sb[j] = int(sxd[((mt0 + j) * quads + (s >> 2)) * 64 + lane] >> shift);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x8 av = i32x8{int(a[i][0]), int(a[i][1]), int(a[i][2]), int(a[i][3]), 0, 0, 0, 0};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const i32x8 bv = i32x8{int(b[j][0]), int(b[j][1]), int(b[j][2]), int(b[j][3]), 0, 0, 0, 0};
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
-        }
-      }
-    } else {
+    {
       // scales: weight side 4 consecutive n x 2 groups per lane, token side 2 groups per lane
       const uint16_t* sw16 = reinterpret_cast<const uint16_t*>(p.sw);
       const uint16_t* sx16 = reinterpret_cast<const uint16_t*>(p.sx);
@@ -349,6 +330,224 @@ __global__ __launch_bounds__(256) void k2_gemm(K2Params p) {
   }
 }
 
+
+// ------------------------------------------------------------ k2_mx (MXFP4)
+// One workgroup = 256 output columns x 256 tokens, 4 waves in a 2 x 2 grid,
+// each 128 x 128 (8 x 8 tiles of 16 x 16, 256 fp32 accumulators per lane).
+// Per 128-deep K step the workgroup stages 16 weight fragments, 16
+// activation fragments and their e8m0 scale dwords (34 KB) in LDS with
+// direct global->LDS loads; MX_STAGES steps are in flight.  Each wave issues
+// 10 of the 40 loads of a step.  The tile order is XCD-aware: consecutive
+// tiles of the grouped order land on the same XCD (and its L2).
+namespace mx {
+constexpr int STAGES = 4;
+constexpr int A_OFF = 0;                 // 16 weight fragments
+constexpr int B_OFF = 16 * 1024;         // 16 activation fragments
+constexpr int SA_OFF = 32 * 1024;        // 4 weight scale dwords x 64 lanes
+constexpr int SB_OFF = 32 * 1024 + 1024; // 4 activation scale dwords x 64 lanes
+constexpr int STAGE_BYTES = 34 * 1024;
+constexpr int GROUP_M = 8;               // m-tiles per group of the tile order
+}  // namespace mx
+
+struct MxParams {
+  const uint8_t* wq;
+  const uint8_t* sw;
+  const uint16_t* l2;
+  const float* bias;
+  const uint8_t* xq;
+  const uint8_t* sx;
+  const uint16_t* t;
+  uint16_t* Y;
+  int64_t ldy, M, N, K;
+  int slots, nchunks;
+  int tiles_n, tiles_m;
+};
+
+
+// Scaled FP4 MFMA with the scale bytes picked by op_sel; oa / ob are
+// compile-time constants at every call site (unrolled loops), so the switch folds.
+__device__ __forceinline__ f32x4 mfma_mx(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb, int oa, int ob) {
+#define SVDQ_MX_CASE(OA, OB) \
+  case OA * 4 + OB: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OA, sa, OB, sb);
+  switch (oa * 4 + ob) {
+    SVDQ_MX_CASE(0, 0) SVDQ_MX_CASE(0, 1) SVDQ_MX_CASE(0, 2) SVDQ_MX_CASE(0, 3)
+    SVDQ_MX_CASE(1, 0) SVDQ_MX_CASE(1, 1) SVDQ_MX_CASE(1, 2) SVDQ_MX_CASE(1, 3)
+    SVDQ_MX_CASE(2, 0) SVDQ_MX_CASE(2, 1) SVDQ_MX_CASE(2, 2) SVDQ_MX_CASE(2, 3)
+    SVDQ_MX_CASE(3, 0) SVDQ_MX_CASE(3, 1) SVDQ_MX_CASE(3, 2) SVDQ_MX_CASE(3, 3)
+    default: return c;
+  }
+#undef SVDQ_MX_CASE
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* glb_ptr_t;
+
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt unconstrained
+#define SVDQ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt unconstrained
+#define SVDQ_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4))
+
+template <int DT, bool GELU>
+__global__ __launch_bounds__(256) void k2_mx(MxParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+
+  // XCD-aware tile index: workgroups are dealt to the 8 XCDs round robin, so
+  // give XCD x a contiguous range of the tile order.
+  const int T = p.tiles_n * p.tiles_m;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, kx = bid >> 3, per = T >> 3, rem = T & 7;
+  const int tile = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int gsz_full = mx::GROUP_M * p.tiles_n;
+  const int grp = tile / gsz_full, first_m = grp * mx::GROUP_M;
+  const int gm = (p.tiles_m - first_m) < mx::GROUP_M ? (p.tiles_m - first_m) : mx::GROUP_M;
+  const int within = tile - grp * gsz_full;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int64_t n0 = int64_t(tn) * 256, m0 = int64_t(tm) * 256;
+  const int nsteps = int(p.K / KSTEP);
+  const int64_t nfr = p.N / 16;            // valid weight fragment rows
+
+  // this wave's share of every stage: weight frags 4w..4w+3, activation
+  // frags 4w..4w+3, scale group w of each operand
+  const uint8_t* ga[4];
+  const uint8_t* gb[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    int64_t nt = n0 / 16 + 4 * wave + f;
+    nt = nt < nfr ? nt : nfr - 1;            // a partial last tile re-reads a valid fragment
+    ga[f] = p.wq + (nt * nsteps) * 1024 + lane * 16;
+    gb[f] = p.xq + ((m0 / 16 + 4 * wave + f) * nsteps) * 1024 + lane * 16;
+  }
+  int64_t sgn = n0 / 64 + wave;
+  sgn = sgn < p.N / 64 ? sgn : p.N / 64 - 1;
+  const uint8_t* gsa = p.sw + (sgn * nsteps) * 256 + lane * 4;
+  const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
+
+  auto issue = [&](int s, int st) {
+    uint8_t* base = smem + st * mx::STAGE_BYTES;
+#pragma unroll
+    for (int f = 0; f < 4; ++f) lds_load16(ga[f] + int64_t(s) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) lds_load16(gb[f] + int64_t(s) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
+    lds_load4(gsa + int64_t(s) * 256, base + mx::SA_OFF + wave * 256);
+    lds_load4(gsb + int64_t(s) * 256, base + mx::SB_OFF + wave * 256);
+  };
+
+  f32x4 acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // fragments of one step in registers (double-buffered across steps)
+  struct Frags {
+    u32x4 a[8], b[8];
+    int sa0, sa1, sb0, sb1;
+  };
+  auto read_frags = [&](Frags& F, int st) {
+    const uint8_t* base = smem + st * mx::STAGE_BYTES;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) F.b[j] = *reinterpret_cast<const u32x4*>(base + mx::B_OFF + (8 * wm + j) * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) F.a[i] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + (8 * wn + i) * 1024 + lane * 16);
+    F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
+    F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
+    F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
+    F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+  };
+  auto compute = [&](const Frags& F) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const i32x8 a = i32x8{int(F.a[i][0]), int(F.a[i][1]), int(F.a[i][2]), int(F.a[i][3]), 0, 0, 0, 0};
+      const int sa = i < 4 ? F.sa0 : F.sa1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const i32x8 b = i32x8{int(F.b[j][0]), int(F.b[j][1]), int(F.b[j][2]), int(F.b[j][3]), 0, 0, 0, 0};
+        const int sb = j < 4 ? F.sb0 : F.sb1;
+        acc[i][j] = mfma_mx(a, b, acc[i][j], sa, sb, i & 3, j & 3);
+      }
+    }
+  };
+  // Iteration s: wait until step s+1 is in LDS (its own loads, then the
+  // barrier for everyone's), refill the stage step s-1 used with step s+3,
+  // start reading step s+1's fragments, and run step s's 64 MFMAs meanwhile.
+  auto body = [&](int s, Frags& cur, Frags& nxt) {
+    // cur's LDS reads were issued an iteration ago; retire them here so the
+    // 18 reads below need no counter slot (lgkmcnt counts at most 15)
+    SVDQ_WAIT_LGKM0();
+    if (s + 1 < nsteps) {
+      if (s + 2 < nsteps) SVDQ_WAIT_VM(10);
+      else SVDQ_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      if (s + mx::STAGES - 1 < nsteps) issue(s + mx::STAGES - 1, (s + mx::STAGES - 1) % mx::STAGES);
+      read_frags(nxt, (s + 1) % mx::STAGES);
+    }
+    compute(cur);
+  };
+
+#pragma unroll
+  for (int s = 0; s < mx::STAGES - 1; ++s)
+    if (s < nsteps) issue(s, s);
+  if (nsteps > 2) SVDQ_WAIT_VM(20);
+  else if (nsteps > 1) SVDQ_WAIT_VM(10);
+  else SVDQ_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();
+  Frags F0, F1;
+  read_frags(F0, 0);
+  for (int s = 0; s < nsteps; s += 2) {
+    body(s, F0, F1);
+    if (s + 1 < nsteps) body(s + 1, F1, F0);
+  }
+
+  // epilogue: + T L2 (16-bit MFMA), + bias, GELU, round, store
+  const u32x4* l2 = reinterpret_cast<const u32x4*>(p.l2);
+  const u32x4* tt = reinterpret_cast<const u32x4*>(p.t);
+  const int64_t ntw = n0 / 16 + 8 * wn, mtw = m0 / 16 + 8 * wm;
+  for (int c = 0; c < p.nchunks; ++c) {
+    u32x4 tb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tb[j] = tt[((mtw + j) * (p.slots / 32) + c) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int64_t nt = ntw + i;
+      nt = nt < nfr ? nt : nfr - 1;
+      const u32x4 la = l2[(nt * (p.slots / 32) + c) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16<DT>(la, tb[j], acc[i][j]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t n = n0 + 128 * wn + 16 * i + 4 * q;
+    if (n >= p.N) continue;
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t m = m0 + 128 * wm + 16 * j + (lane & 15);
+      if (m < p.M) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][j][r] + bv[r];
+          if constexpr (GELU) v[r] = gelu_erf(v[r]);
+        }
+        const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
+        const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
+        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{lo, hi};
+      }
+    }
+  }
+}
+
 // -------------------------------------------------- INT4 per-group products
 struct PartialParams {
   const uint8_t* wq;
@@ -402,11 +601,23 @@ void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
   hipLaunchKernelGGL((k1_act<FMT, DT>), dim3(unsigned(Mp / 16)), dim3(256), 0, st, kp);
 }
 
-template <int FMT, int DT>
-void launch_k2(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
+template <int DT>
+void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
-  if (gelu) hipLaunchKernelGGL((k2_gemm<FMT, DT, true>), grid, dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL((k2_gemm<FMT, DT, false>), grid, dim3(256), 0, st, kp);
+  if (gelu) hipLaunchKernelGGL((k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
+  else hipLaunchKernelGGL((k2_int4<DT, false>), grid, dim3(256), 0, st, kp);
+}
+
+template <int DT>
+void launch_k2_mx(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
+  MxParams mp;
+  mp.wq = kp.wq; mp.sw = kp.sw; mp.l2 = kp.l2; mp.bias = kp.bias; mp.xq = kp.xq; mp.sx = kp.sx; mp.t = kp.t;
+  mp.Y = kp.Y; mp.ldy = kp.ldy; mp.M = kp.M; mp.N = kp.N; mp.K = kp.K; mp.slots = kp.slots; mp.nchunks = kp.nchunks;
+  mp.tiles_n = int(svdq::ceil_div(kp.N, 256));
+  mp.tiles_m = int(Mp / 256);
+  dim3 grid(unsigned(mp.tiles_n * mp.tiles_m));
+  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), grid, dim3(256), 0, st, mp);
+  else hipLaunchKernelGGL((k2_mx<DT, false>), grid, dim3(256), 0, st, mp);
 }
 
 svdq_status check_device_layer(const svdq_layer* L) {
@@ -476,11 +687,11 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
   kp.nchunks = int(svdq::ceil_div(L->rank_active, 32));
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
   if (L->fmt == SVDQ_FMT_INT4_G64) {
-    if (L->dtype == SVDQ_BF16) launch_k2<SVDQ_FMT_INT4_G64, SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2<SVDQ_FMT_INT4_G64, SVDQ_F16>(kp, w.Mp, gelu, stream);
+    if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
+    else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
   } else {
-    if (L->dtype == SVDQ_BF16) launch_k2<SVDQ_FMT_MXFP4_G32, SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2<SVDQ_FMT_MXFP4_G32, SVDQ_F16>(kp, w.Mp, gelu, stream);
+    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w.Mp, gelu, stream);
+    else launch_k2_mx<SVDQ_F16>(kp, w.Mp, gelu, stream);
   }
   return launch_ok();
 }

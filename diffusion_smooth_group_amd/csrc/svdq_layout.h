@@ -44,7 +44,7 @@ struct BlobOffsets {
 
 // bytes of the weight scales
 inline size_t weight_scale_bytes(int64_t K, int64_t N, int fmt) {
-  if (fmt == 1) return size_t(N / 16) * size_t(ceil_div(K, 512)) * 64 * 4;   // MX: 4 steps per dword
+  if (fmt == 1) return size_t(N) * size_t(K / 32);                          // MX: one byte per 32-block
   return size_t(N / 16) * size_t(K / KSTEP) * 64;                           // INT4: 2 groups x 16 rows x fp16
 }
 
@@ -68,7 +68,7 @@ struct WsOffsets {
 };
 
 inline size_t act_scale_bytes(int64_t Mp, int64_t K, int fmt) {
-  if (fmt == 1) return size_t(Mp / 16) * size_t(ceil_div(K, 512)) * 64 * 4;
+  if (fmt == 1) return size_t(Mp) * size_t(K / 32);
   return size_t(Mp / 16) * size_t(K / KSTEP) * 64;
 }
 
@@ -104,12 +104,14 @@ inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int
   *byte = size_t(((t * (K / KSTEP) + s) * 64 + lane) * 16 + b);
 }
 
-// MX e8m0 scale of (row r, 32-block b): byte offset.
+// MX e8m0 scale of (row r, 32-block b): byte offset.  Per (group of four
+// 16-row tiles, step): 64 lanes x 4 bytes; lane l holds the scale of its
+// fragment row and K quarter, byte i of the dword belongs to tile 4g + i
+// (the scaled MFMA selects it with op_sel).
 inline size_t mx_scale_pos(int64_t r, int64_t b, int64_t K) {
   int64_t t = r / 16, s = b / 4, q = b % 4;
   int64_t lane = (r % 16) + 16 * q;
-  int64_t quads = ceil_div(K, 512);
-  return size_t(((t * quads + s / 4) * 64 + lane) * 4 + (s % 4));
+  return size_t((((t / 4) * (K / KSTEP) + s) * 64 + lane) * 4 + (t % 4));
 }
 
 // INT4 fp16 scale of weight (column n, 64-group G): element (uint16) offset.

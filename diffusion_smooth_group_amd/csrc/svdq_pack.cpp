@@ -17,7 +17,7 @@
 #include <cstring>
 #include <vector>
 
-#include "../../include/svdq.h"
+#include "svdq.h"
 #include "svdq_host.h"
 #include "svdq_layout.h"
 
