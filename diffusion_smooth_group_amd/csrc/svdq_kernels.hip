@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void k1_act(K1Params p) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
 
-    uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
     if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+      uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
       amax = fmaxf(amax, __shfl_xor(amax, 16));            // the 64-group spans lanes q and q^1
       float sc = fminf(amax / 7.0f, 65504.0f);
       const unsigned sh = f2h<SVDQ_F16>(sc);
@@ -165,9 +165,14 @@ __global__ __launch_bounds__(256) void k1_act(K1Params p) {
         const unsigned c = e2m1_index(fabsf(u)) | ((__float_as_uint(xh[i]) >> 28) & 8u);
         d[i >> 3] |= c << (4 * (i & 7));
       }
-      *reinterpret_cast<u32x4*>(frag + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
-      // byte (mt % 4) of the dword of tile group mt / 4 (selected by op_sel in the GEMM)
-      p.sx[((size_t(mt >> 2) * nsteps + s) * 64 + lane) * 4 + (mt & 3)] = (uint8_t)e;
+      // 32-row fragment tile t32 = mt / 2; K block q of the step -> half q / 2,
+      // lane (row in the 32-tile) + 32 (q % 2)
+      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+      const int l32 = r32 + 32 * (q & 1), h = q >> 1;
+      uint8_t* frag32 = p.xq + ((size_t(t32) * nsteps + s) * 2 + h) * 1024;
+      *reinterpret_cast<u32x4*>(frag32 + l32 * 16) = u32x4{d[0], d[1], d[2], d[3]};
+      // scale byte 2 (t32 % 2) + h of the dword of the 32-tile pair (op_sel in the GEMM)
+      p.sx[((size_t(t32 >> 1) * nsteps + s) * 64 + l32) * 4 + 2 * (t32 & 1) + h] = (uint8_t)e;
     }
 
     // down-projection T^T += L1x^T X^T on the raw 16-bit inputs
@@ -195,12 +200,18 @@ __global__ __launch_bounds__(256) void k1_act(K1Params p) {
 #pragma unroll
     for (int w = 1; w < 4; ++w) v += red[w][jt][lane];
     // lane holds T[m][16 jt + 4q + i]; place it in the epilogue's B-fragment order
-    const int c = jt >> 1;
-    const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
-    const int e0 = 4 * (q & 1);
     const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
     const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
-    uint16_t* dst = p.t + ((size_t(mt) * (p.slots / 32) + c) * 64 + ldst) * 8 + e0;
+    uint16_t* dst;
+    if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
+      // 32-row tiles, 16-rank chunks: lane (row in tile) + 32 (j % 16 >= 8)
+      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+      dst = p.t + ((size_t(t32) * (p.slots / 16) + jt) * 64 + r32 + 32 * (q >> 1)) * 8 + 4 * (q & 1);
+    } else {
+      // 16-row tiles, 32-rank chunks
+      const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
+      dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
+    }
     *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
   }
 }
@@ -216,7 +227,7 @@ struct K2Params {
   const uint16_t* t;
   uint16_t* Y;
   int64_t ldy, M, N, K;
-  int slots, nchunks;
+  int slots, nchunks, nchunks16;
 };
 
 __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
@@ -333,21 +344,27 @@ __global__ __launch_bounds__(256) void k2_int4(K2Params p) {
 
 // ------------------------------------------------------------ k2_mx (MXFP4)
 // One workgroup = 256 output columns x 256 tokens, 4 waves in a 2 x 2 grid,
-// each 128 x 128 (8 x 8 tiles of 16 x 16, 256 fp32 accumulators per lane).
-// Per 128-deep K step the workgroup stages 16 weight fragments, 16
-// activation fragments and their e8m0 scale dwords (34 KB) in LDS with
-// direct global->LDS loads; MX_STAGES steps are in flight.  Each wave issues
-// 10 of the 40 loads of a step.  The tile order is XCD-aware: consecutive
-// tiles of the grouped order land on the same XCD (and its L2).
+// each 128 x 128 = 4 x 4 tiles of 32 x 32 on V_MFMA_SCALE_F32_32X32X64_F8F6F4
+// (16 fp32 accumulators per tile and lane, 256 in all).  Per 128-deep K
+// step the workgroup stages 8 weight and 8 activation fragment tiles (2 KB
+// each) and their e8m0 scale dwords (34 KB) in LDS with direct global->LDS
+// loads; mx::STAGES steps are in flight and the fragments of the next step
+// are read into registers while the current step's 32 MFMAs run.  The tile
+// order is XCD-aware: consecutive tiles of a grouped order share an XCD's L2.
+// The epilogue adds T L2 (32 x 32 x 16 bf16/f16 MFMA), bias and GELU, rounds,
+// and writes the tile through LDS so every global store covers whole rows.
 namespace mx {
 constexpr int STAGES = 4;
-constexpr int A_OFF = 0;                 // 16 weight fragments
-constexpr int B_OFF = 16 * 1024;         // 16 activation fragments
+constexpr int A_OFF = 0;                 // 8 weight tiles x 2 halves x 1 KB
+constexpr int B_OFF = 16 * 1024;         // 8 activation tiles x 2 halves x 1 KB
 constexpr int SA_OFF = 32 * 1024;        // 4 weight scale dwords x 64 lanes
 constexpr int SB_OFF = 32 * 1024 + 1024; // 4 activation scale dwords x 64 lanes
 constexpr int STAGE_BYTES = 34 * 1024;
 constexpr int GROUP_M = 8;               // m-tiles per group of the tile order
+constexpr int OUT_PITCH = 272;           // bytes per staged output row (128 x 2 + 16)
+constexpr int BIAS_BYTES = 1024;         // the workgroup's 256 bias values, after the ring
 }  // namespace mx
+static_assert(4 * 128 * mx::OUT_PITCH <= mx::STAGES * mx::STAGE_BYTES, "output staging must fit the LDS ring");
 
 struct MxParams {
   const uint8_t* wq;
@@ -359,16 +376,17 @@ struct MxParams {
   const uint16_t* t;
   uint16_t* Y;
   int64_t ldy, M, N, K;
-  int slots, nchunks;
+  int slots, nchunks16;
   int tiles_n, tiles_m;
 };
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Scaled FP4 MFMA with the scale bytes picked by op_sel; oa / ob are
+// Scaled FP4 32x32x64 MFMA with the scale bytes picked by op_sel; oa / ob are
 // compile-time constants at every call site (unrolled loops), so the switch folds.
-__device__ __forceinline__ f32x4 mfma_mx(const i32x8& a, const i32x8& b, f32x4 c, int sa, int sb, int oa, int ob) {
+__device__ __forceinline__ f32x16 mfma_mx32(const i32x8& a, const i32x8& b, f32x16 c, int sa, int sb, int oa, int ob) {
 #define SVDQ_MX_CASE(OA, OB) \
-  case OA * 4 + OB: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, OA, sa, OB, sb);
+  case OA * 4 + OB: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, OA, sa, OB, sb);
   switch (oa * 4 + ob) {
     SVDQ_MX_CASE(0, 0) SVDQ_MX_CASE(0, 1) SVDQ_MX_CASE(0, 2) SVDQ_MX_CASE(0, 3)
     SVDQ_MX_CASE(1, 0) SVDQ_MX_CASE(1, 1) SVDQ_MX_CASE(1, 2) SVDQ_MX_CASE(1, 3)
@@ -377,6 +395,14 @@ __device__ __forceinline__ f32x4 mfma_mx(const i32x8& a, const i32x8& b, f32x4 c
     default: return c;
   }
 #undef SVDQ_MX_CASE
+}
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32x16(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (DT == SVDQ_BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -396,9 +422,9 @@ __device__ __forceinline__ void lds_load4(const void* g, void* l) {
 
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int q = lane >> 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES + mx::BIAS_BYTES];
+  // the wave index is uniform: keep it (and every LDS address derived from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
 
   // XCD-aware tile index: workgroups are dealt to the 8 XCDs round robin, so
@@ -414,136 +440,252 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   const int tm = first_m + within % gm, tn = within / gm;
   const int64_t n0 = int64_t(tn) * 256, m0 = int64_t(tm) * 256;
   const int nsteps = int(p.K / KSTEP);
-  const int64_t nfr = p.N / 16;            // valid weight fragment rows
+  const int64_t ntiles_n = p.N / 32;       // valid 32-row weight tiles
+  // After the K steps come "low-rank steps": each stages two 16-rank chunks
+  // of L2 (weight side) and T (token side) through the same pipeline, and
+  // runs the up-projection on the 16-bit MFMA into the same accumulators.
+  const int lr_steps = (p.nchunks16 + 1) / 2;
+  const int total = nsteps + lr_steps;
+  const int cs = p.slots / 16;              // 16-rank chunks per tile in L2 / T
 
-  // this wave's share of every stage: weight frags 4w..4w+3, activation
-  // frags 4w..4w+3, scale group w of each operand
+  // this wave's share of every stage: weight units 4w..4w+3 and token units
+  // 4w..4w+3 (unit u = tile u / 2, half (or chunk) u % 2), scale group w of each
+  int64_t tA[4], tB[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    const int u = 4 * wave + f;
+    int64_t nt = n0 / 32 + u / 2;
+    tA[f] = nt < ntiles_n ? nt : ntiles_n - 1;   // a partial last tile re-reads a valid tile
+    tB[f] = m0 / 32 + u / 2;
+  }
+  int64_t pn = n0 / 64 + wave;
+  pn = pn < p.N / 64 ? pn : p.N / 64 - 1;
+  const uint8_t* gsa = p.sw + (pn * nsteps) * 256 + lane * 4;
+  const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
+  const uint8_t* l2b = reinterpret_cast<const uint8_t*>(p.l2) + lane * 16;
+  const uint8_t* ttb = reinterpret_cast<const uint8_t*>(p.t) + lane * 16;
+
+  // this wave's fixed source addresses; a K step q adds q * 2048 (fragments)
+  // or q * 256 (scales)
   const uint8_t* ga[4];
   const uint8_t* gb[4];
 #pragma unroll
   for (int f = 0; f < 4; ++f) {
-    int64_t nt = n0 / 16 + 4 * wave + f;
-    nt = nt < nfr ? nt : nfr - 1;            // a partial last tile re-reads a valid fragment
-    ga[f] = p.wq + (nt * nsteps) * 1024 + lane * 16;
-    gb[f] = p.xq + ((m0 / 16 + 4 * wave + f) * nsteps) * 1024 + lane * 16;
+    const int h = (4 * wave + f) & 1;
+    ga[f] = p.wq + (tA[f] * nsteps * 2 + h) * 1024 + lane * 16;
+    gb[f] = p.xq + (tB[f] * nsteps * 2 + h) * 1024 + lane * 16;
   }
-  int64_t sgn = n0 / 64 + wave;
-  sgn = sgn < p.N / 64 ? sgn : p.N / 64 - 1;
-  const uint8_t* gsa = p.sw + (sgn * nsteps) * 256 + lane * 4;
-  const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
-
-  auto issue = [&](int s, int st) {
+  // one of the 10 loads a wave issues per K step
+  auto issue_unit = [&](int q, uint8_t* base, int x) {
+    if (x < 4) lds_load16(ga[x] + int64_t(q) * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
+    else if (x < 8) lds_load16(gb[x - 4] + int64_t(q) * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
+    else if (x == 8) lds_load4(gsa + int64_t(q) * 256, base + mx::SA_OFF + wave * 256);
+    else lds_load4(gsb + int64_t(q) * 256, base + mx::SB_OFF + wave * 256);
+  };
+  // the 10 loads of low-rank step e: chunks 2e, 2e+1 of L2 and T (the scale
+  // slots reload step 0's scales so every step issues 10 loads)
+  auto issue_lr = [&](int e, uint8_t* base) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int h = (4 * wave + f) & 1;
+      int c = 2 * e + h;
+      c = c < p.nchunks16 ? c : p.nchunks16 - 1;
+      lds_load16(l2b + (tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
+      lds_load16(ttb + (tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
+    }
+    lds_load4(gsa, base + mx::SA_OFF + wave * 256);
+    lds_load4(gsb, base + mx::SB_OFF + wave * 256);
+  };
+  auto issue = [&](int q, int st) {
     uint8_t* base = smem + st * mx::STAGE_BYTES;
+    if (q < nsteps) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) lds_load16(ga[f] + int64_t(s) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
-#pragma unroll
-    for (int f = 0; f < 4; ++f) lds_load16(gb[f] + int64_t(s) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
-    lds_load4(gsa + int64_t(s) * 256, base + mx::SA_OFF + wave * 256);
-    lds_load4(gsb + int64_t(s) * 256, base + mx::SB_OFF + wave * 256);
+      for (int x = 0; x < 10; ++x) issue_unit(q, base, x);
+    } else {
+      issue_lr(q - nsteps, base);
+    }
   };
 
-  f32x4 acc[8][8];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // fragments of one step in registers (double-buffered across steps)
   struct Frags {
-    u32x4 a[8], b[8];
+    u32x4 a[4][2], b[4][2];
     int sa0, sa1, sb0, sb1;
   };
   auto read_frags = [&](Frags& F, int st) {
     const uint8_t* base = smem + st * mx::STAGE_BYTES;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) F.b[j] = *reinterpret_cast<const u32x4*>(base + mx::B_OFF + (8 * wm + j) * 1024 + lane * 16);
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) F.a[i] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + (8 * wn + i) * 1024 + lane * 16);
+      for (int h = 0; h < 2; ++h)
+        F.b[j][h] = *reinterpret_cast<const u32x4*>(base + mx::B_OFF + ((4 * wm + j) * 2 + h) * 1024 + lane * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        F.a[i][h] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + ((4 * wn + i) * 2 + h) * 1024 + lane * 16);
     F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
     F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
     F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
     F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
   };
+  // One MFMA of a K step (k = 0..31 walks h, i, j; the two halves of a
+  // tile's K are 16 MFMAs apart, so no MFMA waits on its predecessor).
+  auto mfma_k = [&](const Frags& F, int k) {
+    const int h = k >> 4, i = (k >> 2) & 3, j = k & 3;
+    const i32x8 a = i32x8{int(F.a[i][h][0]), int(F.a[i][h][1]), int(F.a[i][h][2]), int(F.a[i][h][3]), 0, 0, 0, 0};
+    const i32x8 b = i32x8{int(F.b[j][h][0]), int(F.b[j][h][1]), int(F.b[j][h][2]), int(F.b[j][h][3]), 0, 0, 0, 0};
+    acc[i][j] = mfma_mx32(a, b, acc[i][j], i < 2 ? F.sa0 : F.sa1, j < 2 ? F.sb0 : F.sb1, 2 * (i & 1) + h, 2 * (j & 1) + h);
+  };
   auto compute = [&](const Frags& F) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const i32x8 a = i32x8{int(F.a[i][0]), int(F.a[i][1]), int(F.a[i][2]), int(F.a[i][3]), 0, 0, 0, 0};
-      const int sa = i < 4 ? F.sa0 : F.sa1;
+    for (int k = 0; k < 32; ++k) mfma_k(F, k);
+  };
+  // up-projection of low-rank step e: chunks 2e, 2e+1 of T L2
+  auto compute_lr = [&](int e, const Frags& F) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const i32x8 b = i32x8{int(F.b[j][0]), int(F.b[j][1]), int(F.b[j][2]), int(F.b[j][3]), 0, 0, 0, 0};
-        const int sb = j < 4 ? F.sb0 : F.sb1;
-        acc[i][j] = mfma_mx(a, b, acc[i][j], sa, sb, i & 3, j & 3);
+    for (int h = 0; h < 2; ++h)
+      if (2 * e + h < p.nchunks16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x16<DT>(F.a[i][h], F.b[j][h], acc[i][j]);
       }
+  };
+  // Memory op k of the next step, placed after MFMA k: 8 token and 8 weight
+  // fragment reads, the 4 scale reads, then the 10 loads of step s + 3.
+  auto mem_k = [&](Frags& nxt, const uint8_t* rb, uint8_t* lb, int s3, int k) {
+    if (k < 8) {
+      nxt.b[k >> 1][k & 1] = *reinterpret_cast<const u32x4*>(rb + mx::B_OFF + ((4 * wm + (k >> 1)) * 2 + (k & 1)) * 1024 + lane * 16);
+    } else if (k < 16) {
+      const int kk = k - 8;
+      nxt.a[kk >> 1][kk & 1] = *reinterpret_cast<const u32x4*>(rb + mx::A_OFF + ((4 * wn + (kk >> 1)) * 2 + (kk & 1)) * 1024 + lane * 16);
+    } else if (k == 16) {
+      nxt.sb0 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
+      nxt.sb1 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
+    } else if (k == 17) {
+      nxt.sa0 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
+      nxt.sa1 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+    } else if (k < 28) {
+      issue_unit(s3, lb, k - 18);
     }
   };
   // Iteration s: wait until step s+1 is in LDS (its own loads, then the
-  // barrier for everyone's), refill the stage step s-1 used with step s+3,
-  // start reading step s+1's fragments, and run step s's 64 MFMAs meanwhile.
-  auto body = [&](int s, Frags& cur, Frags& nxt) {
+  // barrier for everyone's), then run step s's 32 MFMAs with the reads of
+  // step s+1 and the refill of the stage step s-1 used (with step s+3)
+  // placed between them, fenced so the compiler keeps that order.
+  auto body_full = [&](int s, Frags& cur, Frags& nxt) {   // needs s + 3 < nsteps
     // cur's LDS reads were issued an iteration ago; retire them here so the
-    // 18 reads below need no counter slot (lgkmcnt counts at most 15)
+    // 20 reads below need no counter slot (lgkmcnt counts at most 15)
+    SVDQ_WAIT_LGKM0();
+    SVDQ_WAIT_VM(10);
+    __builtin_amdgcn_s_barrier();
+    const uint8_t* rb = smem + ((s + 1) & 3) * mx::STAGE_BYTES;
+    uint8_t* lb = smem + ((s + 3) & 3) * mx::STAGE_BYTES;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      mfma_k(cur, k);
+      mem_k(nxt, rb, lb, s + 3, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the last K steps: wait for step s+1 (if it is a K step), refill, read,
+  // compute step s
+  auto body_tail = [&](int s, Frags& cur, Frags& nxt) {
     SVDQ_WAIT_LGKM0();
     if (s + 1 < nsteps) {
-      if (s + 2 < nsteps) SVDQ_WAIT_VM(10);
+      if (s + 2 < total) SVDQ_WAIT_VM(10);
       else SVDQ_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();
-      if (s + mx::STAGES - 1 < nsteps) issue(s + mx::STAGES - 1, (s + mx::STAGES - 1) % mx::STAGES);
-      read_frags(nxt, (s + 1) % mx::STAGES);
+      if (s + 3 < total) issue(s + 3, (s + 3) & 3);
+      read_frags(nxt, (s + 1) & 3);
     }
     compute(cur);
   };
+  static_assert(mx::STAGES == 4, "the step bookkeeping assumes a 4-stage ring");
 
+  // bias of the workgroup's 256 columns, staged once (64 floats per wave)
+  float* bias_lds = reinterpret_cast<float*>(smem + mx::STAGES * mx::STAGE_BYTES);
+  {
+    int64_t nb = n0 + 64 * wave + lane;
+    nb = nb < p.N ? nb : p.N - 1;
+    lds_load4(p.bias + nb, bias_lds + 64 * wave);
+  }
 #pragma unroll
   for (int s = 0; s < mx::STAGES - 1; ++s)
-    if (s < nsteps) issue(s, s);
-  if (nsteps > 2) SVDQ_WAIT_VM(20);
-  else if (nsteps > 1) SVDQ_WAIT_VM(10);
+    if (s < total) issue(s, s);
+  if (total > 2) SVDQ_WAIT_VM(20);
+  else if (total > 1) SVDQ_WAIT_VM(10);
   else SVDQ_WAIT_VM(0);
   __builtin_amdgcn_s_barrier();
   Frags F0, F1;
   read_frags(F0, 0);
-  for (int s = 0; s < nsteps; s += 2) {
-    body(s, F0, F1);
-    if (s + 1 < nsteps) body(s + 1, F1, F0);
+  int s = 0;
+  for (; s + 4 < nsteps; s += 2) {       // steady state: every step issued is a K step
+    body_full(s, F0, F1);
+    body_full(s + 1, F1, F0);
+  }
+  for (; s < nsteps; s += 2) {
+    body_tail(s, F0, F1);
+    if (s + 1 < nsteps) body_tail(s + 1, F1, F0);
+  }
+  // low-rank steps (their loads were issued during the last K steps)
+  for (int q = nsteps; q < total; ++q) {
+    SVDQ_WAIT_LGKM0();
+    SVDQ_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    if (q + 3 < total) issue(q + 3, (q + 3) & 3);
+    Frags F;
+    read_frags(F, q & 3);
+    SVDQ_WAIT_LGKM0();
+    compute_lr(q - nsteps, F);
   }
 
-  // epilogue: + T L2 (16-bit MFMA), + bias, GELU, round, store
-  const u32x4* l2 = reinterpret_cast<const u32x4*>(p.l2);
-  const u32x4* tt = reinterpret_cast<const u32x4*>(p.t);
-  const int64_t ntw = n0 / 16 + 8 * wn, mtw = m0 / 16 + 8 * wm;
-  for (int c = 0; c < p.nchunks; ++c) {
-    u32x4 tb[8];
+  // epilogue: bias, GELU, round; stage the wave's 128 x 128 tile in LDS as
+  // [token][column] rows, then store whole 256-byte row segments
+  SVDQ_WAIT_LGKM0();
+  SVDQ_WAIT_VM(0);
+  __syncthreads();                       // every wave is done with the LDS ring
+  uint8_t* ob = smem + wave * (128 * mx::OUT_PITCH);
+  const int64_t nw = n0 + 128 * wn;      // first column of this wave's tile
 #pragma unroll
-    for (int j = 0; j < 8; ++j) tb[j] = tt[((mtw + j) * (p.slots / 32) + c) * 64 + lane];
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int64_t nt = ntw + i;
-      nt = nt < nfr ? nt : nfr - 1;
-      const u32x4 la = l2[(nt * (p.slots / 32) + c) * 64 + lane];
+    for (int g = 0; g < 4; ++g) {
+      // accumulator v = 4g + r of tile (i, j): column 32i + 8g + 4(lane / 32) + r, token 32j + lane % 32
+      const int nl = 32 * i + 8 * g + 4 * (lane >> 5);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_lds + 128 * wn + nl);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) acc[i][j] = mfma16<DT>(la, tb[j], acc[i][j]);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int64_t n = n0 + 128 * wn + 16 * i + 4 * q;
-    if (n >= p.N) continue;
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int64_t m = m0 + 128 * wm + 16 * j + (lane & 15);
-      if (m < p.M) {
+      for (int j = 0; j < 4; ++j) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][r] + bv[r];
+          v[r] = acc[i][j][4 * g + r] + bv[r];
           if constexpr (GELU) v[r] = gelu_erf(v[r]);
         }
         const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
         const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
-        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{lo, hi};
+        const int ml = 32 * j + (lane & 31);
+        *reinterpret_cast<u32x2*>(ob + ml * mx::OUT_PITCH + nl * 2) = u32x2{lo, hi};
       }
+    }
+  }
+  SVDQ_WAIT_LGKM0();
+  if (nw < p.N) {
+    const int64_t mw = m0 + 128 * wm;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int row = 4 * it + (lane >> 4);
+      const int col = (lane & 15) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
+      if (mw + row < p.M) *reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col) = v;
     }
   }
 }
@@ -612,7 +754,8 @@ template <int DT>
 void launch_k2_mx(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   MxParams mp;
   mp.wq = kp.wq; mp.sw = kp.sw; mp.l2 = kp.l2; mp.bias = kp.bias; mp.xq = kp.xq; mp.sx = kp.sx; mp.t = kp.t;
-  mp.Y = kp.Y; mp.ldy = kp.ldy; mp.M = kp.M; mp.N = kp.N; mp.K = kp.K; mp.slots = kp.slots; mp.nchunks = kp.nchunks;
+  mp.Y = kp.Y; mp.ldy = kp.ldy; mp.M = kp.M; mp.N = kp.N; mp.K = kp.K; mp.slots = kp.slots;
+  mp.nchunks16 = kp.nchunks16;
   mp.tiles_n = int(svdq::ceil_div(kp.N, 256));
   mp.tiles_m = int(Mp / 256);
   dim3 grid(unsigned(mp.tiles_n * mp.tiles_m));
@@ -649,7 +792,8 @@ extern "C" svdq_status svdq_quantize_activations(const svdq_layer* L, const void
   kp.invlam = reinterpret_cast<const float*>(blob + L->off_invlam);
   kp.l1x = reinterpret_cast<const uint16_t*>(blob + L->off_l1x);
   kp.slots = L->rank_slots;
-  kp.njt = 2 * int(svdq::ceil_div(L->rank_active, 32));
+  kp.njt = L->fmt == SVDQ_FMT_MXFP4_G32 ? int(svdq::ceil_div(L->rank_active, 16))
+                                        : 2 * int(svdq::ceil_div(L->rank_active, 32));
   kp.xq = ws + w.xq; kp.sx = ws + w.sx; kp.t = reinterpret_cast<uint16_t*>(ws + w.t);
   if (L->fmt == SVDQ_FMT_INT4_G64) {
     if (L->dtype == SVDQ_BF16) launch_k1<SVDQ_FMT_INT4_G64, SVDQ_BF16>(kp, w.Mp, stream);
@@ -668,7 +812,7 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
   if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
   if (!Y_dev || !ws_dev) return SVDQ_ERR_INVALID_ARG;
-  if (ldy < L->N || ldy % 4 != 0 || !aligned(Y_dev, 8)) return SVDQ_ERR_SHAPE;
+  if (ldy < L->N || ldy % 8 != 0 || !aligned(Y_dev, 16)) return SVDQ_ERR_SHAPE;
   svdq::WsOffsets w = svdq::ws_offsets(M, L->K, L->rank_slots, L->fmt);
   if (ws_bytes < w.total) return SVDQ_ERR_CAPACITY;
   if (!aligned(ws_dev, 256)) return SVDQ_ERR_INVALID_ARG;
@@ -685,6 +829,7 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
   kp.ldy = ldy; kp.M = M; kp.N = L->N; kp.K = L->K;
   kp.slots = L->rank_slots;
   kp.nchunks = int(svdq::ceil_div(L->rank_active, 32));
+  kp.nchunks16 = int(svdq::ceil_div(L->rank_active, 16));
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
   if (L->fmt == SVDQ_FMT_INT4_G64) {
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
@@ -704,7 +849,7 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
   if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
   if (!Y_dev) return SVDQ_ERR_INVALID_ARG;
-  if (ldy < L->N || ldy % 4 != 0 || !aligned(Y_dev, 8)) return SVDQ_ERR_SHAPE;
+  if (ldy < L->N || ldy % 8 != 0 || !aligned(Y_dev, 16)) return SVDQ_ERR_SHAPE;
   st = svdq_quantize_activations(L, X_dev, M, ldx, ws_dev, ws_bytes, stream);
   if (st != SVDQ_OK) return st;
   return svdq_gemm_forward(L, M, Y_dev, ldy, ws_dev, ws_bytes, flags, stream);

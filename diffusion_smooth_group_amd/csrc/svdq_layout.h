@@ -2,15 +2,17 @@
 // workspace.  Shared by the host pack and the device launch code of the
 // library (not by any checker).
 //
-// Every 4-bit operand is stored as matrix-core fragments: for a 16-wide
-// tile of rows (output columns n for the weight, tokens m for activations)
-// and a 128-deep step of K, 64 lanes x 16 bytes.  Lane l covers row
-// (l % 16) and the K quarter q = l / 16 of the step:
-//   MXFP4: the 16 bytes are the 32 E2M1 codes of k in [32q, 32q+32) of the
-//          step (element 2i in the low nibble of byte i) -- one e8m0 block.
-//   INT4:  bytes [0, 8)  hold k in [16q, 16q+16)      (first 64-group),
-//          bytes [8, 16) hold k in [64+16q, 64+16q+16) (second 64-group).
-// A wave then loads a whole fragment with one 16-byte load per lane.
+// Every 4-bit operand is stored as matrix-core fragments: a wave loads a
+// whole fragment with one 16-byte load per lane.  Rows are output columns n
+// for the weight and tokens m for the activations.
+//   MXFP4 (32 x 32 x 64 scaled MFMA): per 32-row tile and 128-deep K step,
+//          2 halves x 64 lanes x 16 bytes; in half h, lane l holds row l % 32
+//          and the 32 E2M1 codes of k in [64h + 32(l / 32), +32) of the step
+//          (element 2i in the low nibble of byte i) -- one e8m0 block.
+//   INT4 (16 x 16 x 64 integer MFMA): per 16-row tile and step, 64 lanes x
+//          16 bytes; lane l holds row l % 16, bytes [0, 8) are k in
+//          [16q, 16q+16) (first 64-group), bytes [8, 16) are k in
+//          [64+16q, 64+16q+16) (second 64-group), q = l / 16.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -88,30 +90,28 @@ inline WsOffsets ws_offsets(int64_t M, int64_t K, int slots, int fmt) {
 // 4-bit code of (row r, k) in a fragment array with K columns: byte offset
 // and nibble (0 = low) within it.
 inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int* nib) {
-  int64_t t = r / 16, s = k / KSTEP, kk = k % KSTEP;
-  int64_t lane, b;
+  const int64_t nsteps = K / KSTEP, s = k / KSTEP, kk = k % KSTEP;
   if (fmt == 1) {
-    int64_t q = kk / 32, c = kk % 32;
-    lane = (r % 16) + 16 * q;
-    b = c / 2;
+    int64_t t = r / 32, b = kk / 32, c = kk % 32, h = b / 2;
+    int64_t lane = (r % 32) + 32 * (b % 2);
+    *byte = size_t(((t * nsteps + s) * 2 + h) * 1024 + lane * 16 + c / 2);
     *nib = int(c % 2);
   } else {
-    int64_t g = kk / 64, w = kk % 64, q = w / 16, c = w % 16;
-    lane = (r % 16) + 16 * q;
-    b = 8 * g + c / 2;
+    int64_t t = r / 16, g = kk / 64, w = kk % 64, q = w / 16, c = w % 16;
+    int64_t lane = (r % 16) + 16 * q;
+    *byte = size_t(((t * nsteps + s) * 64 + lane) * 16 + 8 * g + c / 2);
     *nib = int(c % 2);
   }
-  *byte = size_t(((t * (K / KSTEP) + s) * 64 + lane) * 16 + b);
 }
 
-// MX e8m0 scale of (row r, 32-block b): byte offset.  Per (group of four
-// 16-row tiles, step): 64 lanes x 4 bytes; lane l holds the scale of its
-// fragment row and K quarter, byte i of the dword belongs to tile 4g + i
-// (the scaled MFMA selects it with op_sel).
+// MX e8m0 scale of (row r, 32-block b): byte offset.  Per (pair of 32-row
+// tiles, step): 64 lanes x 4 bytes; lane l holds the scales of its fragment
+// row and K block in both halves of both tiles, byte 2 (tile % 2) + half
+// (the scaled MFMA picks it with op_sel).
 inline size_t mx_scale_pos(int64_t r, int64_t b, int64_t K) {
-  int64_t t = r / 16, s = b / 4, q = b % 4;
-  int64_t lane = (r % 16) + 16 * q;
-  return size_t((((t / 4) * (K / KSTEP) + s) * 64 + lane) * 4 + (t % 4));
+  int64_t t = r / 32, s = b / 4, bb = b % 4, h = bb / 2;
+  int64_t lane = (r % 32) + 32 * (bb % 2);
+  return size_t((((t / 2) * (K / KSTEP) + s) * 64 + lane) * 4 + 2 * (t % 2) + h);
 }
 
 // INT4 fp16 scale of weight (column n, 64-group G): element (uint16) offset.
@@ -129,8 +129,17 @@ inline size_t int4_xscale_pos(int64_t m, int64_t G, int64_t K) {
 }
 
 // 16-bit low-rank operand of the GEMM epilogue: (row r, rank j), rows are
-// n for L2 and m for T.  Per (16-row tile, 32-rank chunk): 64 lanes x 8.
-inline size_t lr_pos(int64_t r, int64_t j, int slots) {
+// n for L2 and m for T.
+//   MXFP4 (32 x 32 x 16 MFMA): per (32-row tile, 16-rank chunk) 64 lanes x 8;
+//          lane l holds row l % 32 and j in [16c + 8(l / 32), +8).
+//   INT4 (16 x 16 x 32 MFMA): per (16-row tile, 32-rank chunk) 64 lanes x 8;
+//          lane l holds row l % 16 and j in [32c + 8(l / 16), +8).
+inline size_t lr_pos(int64_t r, int64_t j, int slots, int fmt) {
+  if (fmt == 1) {
+    int64_t t = r / 32, c = j / 16, jj = j % 16;
+    int64_t lane = (r % 32) + 32 * (jj / 8);
+    return size_t(((t * (slots / 16) + c) * 64 + lane) * 8 + jj % 8);
+  }
   int64_t t = r / 16, c = j / 32, jj = j % 32, q = jj / 8, e = jj % 8;
   int64_t lane = (r % 16) + 16 * q;
   return size_t(((t * (slots / 32) + c) * 64 + lane) * 8 + e);

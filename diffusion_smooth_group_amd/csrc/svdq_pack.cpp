@@ -217,7 +217,7 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
   for (int64_t j = 0; j < K; ++j)
     for (int i = 0; i < rank; ++i) l1t[l1x_pos(j, i, slots)] = l1x[size_t(j) * rank + i];
   for (int i = 0; i < rank; ++i)
-    for (int64_t n = 0; n < N; ++n) l2t[lr_pos(n, i, slots)] = l2q[size_t(i) * N + n];
+    for (int64_t n = 0; n < N; ++n) l2t[lr_pos(n, i, slots, fmt)] = l2q[size_t(i) * N + n];
   std::memcpy(blob + o.invlam, invlam.data(), size_t(K) * 4);
   std::memcpy(blob + o.lam, lam.data(), size_t(K) * 4);
   float* bias = reinterpret_cast<float*>(blob + o.bias);
@@ -325,7 +325,7 @@ svdq_status write_lora(svdq_layer* L, const uint16_t* A, const uint16_t* B, int 
     for (int64_t n = 0; n < L->N; ++n) {
       uint16_t v = 0;
       if (i < rL) v = f64_to_h16_rne(double(alpha) * double(h16_to_f32(B[size_t(i) * L->N + n], L->dtype)), L->dtype);
-      l2t[lr_pos(n, j, slots)] = v;
+      l2t[lr_pos(n, j, slots, L->fmt)] = v;
     }
   }
   svdq_layer nl = *L;
@@ -380,7 +380,7 @@ extern "C" svdq_status svdq_layer_export(const svdq_layer* L, float* lam, float*
   if (l2) {
     uint16_t* o = static_cast<uint16_t*>(l2);
     for (int j = 0; j < ra; ++j)
-      for (int64_t n = 0; n < N; ++n) o[size_t(j) * N + n] = l2t[lr_pos(n, j, slots)];
+      for (int64_t n = 0; n < N; ++n) o[size_t(j) * N + n] = l2t[lr_pos(n, j, slots, L->fmt)];
   }
   const uint8_t* wq = v + L->off_wq;
   if (codes) {
@@ -462,7 +462,7 @@ extern "C" svdq_status svdq_workspace_export(const svdq_layer* L, const void* ws
     uint16_t* o = static_cast<uint16_t*>(t);
     const int ra = L->rank_active;
     for (int64_t m = 0; m < M; ++m)
-      for (int j = 0; j < ra; ++j) o[size_t(m) * ra + j] = tt[lr_pos(m, j, L->rank_slots)];
+      for (int j = 0; j < ra; ++j) o[size_t(m) * ra + j] = tt[lr_pos(m, j, L->rank_slots, L->fmt)];
   }
   return SVDQ_OK;
 }

@@ -141,7 +141,7 @@ svdq_status svdq_workspace_size(const svdq_layer* layer, int64_t M, size_t* byte
  * the activation kernel (smoothing, group quantization, down-projection,
  * one pass over X) and the 4-bit GEMM with the up-projection, bias and
  * optional GELU in its epilogue.  X_dev: M x K (ldx >= K, ldx % 8 == 0,
- * 16-byte aligned); Y_dev: M x N (ldy >= N, ldy % 4 == 0, 8-byte aligned);
+ * 16-byte aligned); Y_dev: M x N (ldy >= N, ldy % 8 == 0, 16-byte aligned);
  * ws_dev: >= svdq_workspace_size bytes, 256-byte aligned.  M >= 0 (M == 0
  * is a no-op).  Asynchronous. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
