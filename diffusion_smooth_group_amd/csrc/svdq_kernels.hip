@@ -64,6 +64,19 @@ __device__ __forceinline__ unsigned f2h(float f) {   // round to nearest even
   }
 }
 
+// two floats -> two 16-bit values (round to nearest even) in one dword, low
+// half first; one v_cvt_pk_{bf16,f16}_f32 on this target
+template <int DT>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  if constexpr (DT == SVDQ_BF16) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, bf16x2_t{(__bf16)a, (__bf16)b});
+  } else {
+    typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, f16x2_t{(_Float16)a, (_Float16)b});
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (DT == SVDQ_BF16)
@@ -237,7 +250,29 @@ __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
                int(d1 & 0xF0F0F0F0u)};
 }
 
-__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// GELU in its exact form x Phi(x) = x/2 erfc(-x/sqrt2), written without
+// branches so an epilogue over many accumulators stays straight-line code.
+// erfc(z), z >= 0, is the Chebyshev fit of Press et al., Numerical Recipes
+// (2nd ed., sec. 6.2, erfcc): t exp(-z^2 + P(t)) with t = 1 / (1 + z/2), a
+// fractional error below 1.2e-7 over all z >= 0.  For x >= 0 the result is
+// x - x/2 erfc(z), for x < 0 it is x/2 erfc(z), with z = |x| / sqrt2.
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.5f, z, 1.0f));
+  float pc = 0.17087277f;
+  pc = __builtin_fmaf(pc, t, -0.82215223f);
+  pc = __builtin_fmaf(pc, t, 1.48851587f);
+  pc = __builtin_fmaf(pc, t, -1.13520398f);
+  pc = __builtin_fmaf(pc, t, 0.27886807f);
+  pc = __builtin_fmaf(pc, t, -0.18628806f);
+  pc = __builtin_fmaf(pc, t, 0.09678418f);
+  pc = __builtin_fmaf(pc, t, 0.37409196f);
+  pc = __builtin_fmaf(pc, t, 1.00002368f);
+  pc = __builtin_fmaf(pc, t, -1.26551223f);
+  const float e = __builtin_fmaf(-z, z, pc) * 1.44269504088896341f;   // in log2 units
+  const float hx = 0.5f * x * (t * __builtin_amdgcn_exp2f(e));        // x/2 erfc(z)
+  return x < 0.0f ? hx : x - hx;
+}
 
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
 // 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).
@@ -351,8 +386,10 @@ __global__ __launch_bounds__(256) void k2_int4(K2Params p) {
 // loads; mx::STAGES steps are in flight and the fragments of the next step
 // are read into registers while the current step's 32 MFMAs run.  The tile
 // order is XCD-aware: consecutive tiles of a grouped order share an XCD's L2.
-// The epilogue adds T L2 (32 x 32 x 16 bf16/f16 MFMA), bias and GELU, rounds,
-// and writes the tile through LDS so every global store covers whole rows.
+// The accumulators start at the bias (one 16-bit MFMA per 32 x 32 tile); the
+// up-projection T L2 runs as extra pipeline steps on the 32 x 32 x 16
+// bf16/f16 MFMA; the epilogue applies GELU if asked, rounds, and writes the
+// tile through LDS so every global store covers whole rows.
 namespace mx {
 constexpr int STAGES = 4;
 constexpr int A_OFF = 0;                 // 8 weight tiles x 2 halves x 1 KB
@@ -362,9 +399,18 @@ constexpr int SB_OFF = 32 * 1024 + 1024; // 4 activation scale dwords x 64 lanes
 constexpr int STAGE_BYTES = 34 * 1024;
 constexpr int GROUP_M = 8;               // m-tiles per group of the tile order
 constexpr int OUT_PITCH = 272;           // bytes per staged output row (128 x 2 + 16)
-constexpr int BIAS_BYTES = 1024;         // the workgroup's 256 bias values, after the ring
 }  // namespace mx
 static_assert(4 * 128 * mx::OUT_PITCH <= mx::STAGES * mx::STAGE_BYTES, "output staging must fit the LDS ring");
+
+// Slot plan of a steady K step (32 MFMAs): global->LDS load d after MFMA
+// 3d + 1, LDS read e in the remaining slots in order.
+__host__ __device__ constexpr int dma_slot(int k) { return (k % 3 == 1 && k <= 28) ? k / 3 : -1; }
+__host__ __device__ constexpr int lds_slot(int k) {
+  int c = 0;
+  for (int i = 0; i < k; ++i) c += dma_slot(i) < 0 ? 1 : 0;
+  return dma_slot(k) < 0 ? c : -1;
+}
+static_assert(dma_slot(28) == 9 && lds_slot(26) == 17, "every load and read has a slot");
 
 struct MxParams {
   const uint8_t* wq;
@@ -381,6 +427,8 @@ struct MxParams {
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // Scaled FP4 32x32x64 MFMA with the scale bytes picked by op_sel; oa / ob are
 // compile-time constants at every call site (unrolled loops), so the switch folds.
@@ -422,270 +470,292 @@ __device__ __forceinline__ void lds_load4(const void* g, void* l) {
 
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES + mx::BIAS_BYTES];
+  // one LDS object (a second one makes the compiler wait for every global->LDS
+  // load before any LDS read)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
   // the wave index is uniform: keep it (and every LDS address derived from it) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
-
-  // XCD-aware tile index: workgroups are dealt to the 8 XCDs round robin, so
-  // give XCD x a contiguous range of the tile order.
-  const int T = p.tiles_n * p.tiles_m;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, kx = bid >> 3, per = T >> 3, rem = T & 7;
-  const int tile = xcd * per + (xcd < rem ? xcd : rem) + kx;
-  const int gsz_full = mx::GROUP_M * p.tiles_n;
-  const int grp = tile / gsz_full, first_m = grp * mx::GROUP_M;
-  const int gm = (p.tiles_m - first_m) < mx::GROUP_M ? (p.tiles_m - first_m) : mx::GROUP_M;
-  const int within = tile - grp * gsz_full;
-  const int tm = first_m + within % gm, tn = within / gm;
-  const int64_t n0 = int64_t(tn) * 256, m0 = int64_t(tm) * 256;
   const int nsteps = int(p.K / KSTEP);
   const int64_t ntiles_n = p.N / 32;       // valid 32-row weight tiles
-  // After the K steps come "low-rank steps": each stages two 16-rank chunks
-  // of L2 (weight side) and T (token side) through the same pipeline, and
-  // runs the up-projection on the 16-bit MFMA into the same accumulators.
-  const int lr_steps = (p.nchunks16 + 1) / 2;
-  const int total = nsteps + lr_steps;
   const int cs = p.slots / 16;              // 16-rank chunks per tile in L2 / T
-
-  // this wave's share of every stage: weight units 4w..4w+3 and token units
-  // 4w..4w+3 (unit u = tile u / 2, half (or chunk) u % 2), scale group w of each
-  int64_t tA[4], tB[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int u = 4 * wave + f;
-    int64_t nt = n0 / 32 + u / 2;
-    tA[f] = nt < ntiles_n ? nt : ntiles_n - 1;   // a partial last tile re-reads a valid tile
-    tB[f] = m0 / 32 + u / 2;
-  }
-  int64_t pn = n0 / 64 + wave;
-  pn = pn < p.N / 64 ? pn : p.N / 64 - 1;
-  const uint8_t* gsa = p.sw + (pn * nsteps) * 256 + lane * 4;
-  const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
-  const uint8_t* l2b = reinterpret_cast<const uint8_t*>(p.l2) + lane * 16;
-  const uint8_t* ttb = reinterpret_cast<const uint8_t*>(p.t) + lane * 16;
-
-  // this wave's fixed source addresses; a K step q adds q * 2048 (fragments)
-  // or q * 256 (scales)
-  const uint8_t* ga[4];
-  const uint8_t* gb[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    const int h = (4 * wave + f) & 1;
-    ga[f] = p.wq + (tA[f] * nsteps * 2 + h) * 1024 + lane * 16;
-    gb[f] = p.xq + (tB[f] * nsteps * 2 + h) * 1024 + lane * 16;
-  }
-  // one of the 10 loads a wave issues per K step
-  auto issue_unit = [&](int q, uint8_t* base, int x) {
-    if (x < 4) lds_load16(ga[x] + int64_t(q) * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
-    else if (x < 8) lds_load16(gb[x - 4] + int64_t(q) * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
-    else if (x == 8) lds_load4(gsa + int64_t(q) * 256, base + mx::SA_OFF + wave * 256);
-    else lds_load4(gsb + int64_t(q) * 256, base + mx::SB_OFF + wave * 256);
-  };
-  // the 10 loads of low-rank step e: chunks 2e, 2e+1 of L2 and T (the scale
-  // slots reload step 0's scales so every step issues 10 loads)
-  auto issue_lr = [&](int e, uint8_t* base) {
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int h = (4 * wave + f) & 1;
-      int c = 2 * e + h;
-      c = c < p.nchunks16 ? c : p.nchunks16 - 1;
-      lds_load16(l2b + (tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
-      lds_load16(ttb + (tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
-    }
-    lds_load4(gsa, base + mx::SA_OFF + wave * 256);
-    lds_load4(gsb, base + mx::SB_OFF + wave * 256);
-  };
-  auto issue = [&](int q, int st) {
-    uint8_t* base = smem + st * mx::STAGE_BYTES;
-    if (q < nsteps) {
-#pragma unroll
-      for (int x = 0; x < 10; ++x) issue_unit(q, base, x);
-    } else {
-      issue_lr(q - nsteps, base);
-    }
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   // fragments of one step in registers (double-buffered across steps)
   struct Frags {
     u32x4 a[4][2], b[4][2];
     int sa0, sa1, sb0, sb1;
   };
-  auto read_frags = [&](Frags& F, int st) {
-    const uint8_t* base = smem + st * mx::STAGE_BYTES;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        F.b[j][h] = *reinterpret_cast<const u32x4*>(base + mx::B_OFF + ((4 * wm + j) * 2 + h) * 1024 + lane * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        F.a[i][h] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + ((4 * wn + i) * 2 + h) * 1024 + lane * 16);
-    F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
-    F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
-    F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
-    F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
-  };
-  // One MFMA of a K step (k = 0..31 walks h, i, j; the two halves of a
-  // tile's K are 16 MFMAs apart, so no MFMA waits on its predecessor).
-  auto mfma_k = [&](const Frags& F, int k) {
-    const int h = k >> 4, i = (k >> 2) & 3, j = k & 3;
-    const i32x8 a = i32x8{int(F.a[i][h][0]), int(F.a[i][h][1]), int(F.a[i][h][2]), int(F.a[i][h][3]), 0, 0, 0, 0};
-    const i32x8 b = i32x8{int(F.b[j][h][0]), int(F.b[j][h][1]), int(F.b[j][h][2]), int(F.b[j][h][3]), 0, 0, 0, 0};
-    acc[i][j] = mfma_mx32(a, b, acc[i][j], i < 2 ? F.sa0 : F.sa1, j < 2 ? F.sb0 : F.sb1, 2 * (i & 1) + h, 2 * (j & 1) + h);
-  };
-  auto compute = [&](const Frags& F) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) mfma_k(F, k);
-  };
-  // up-projection of low-rank step e: chunks 2e, 2e+1 of T L2
-  auto compute_lr = [&](int e, const Frags& F) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (2 * e + h < p.nchunks16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x16<DT>(F.a[i][h], F.b[j][h], acc[i][j]);
-      }
-  };
-  // Memory op k of the next step, placed after MFMA k: 8 token and 8 weight
-  // fragment reads, the 4 scale reads, then the 10 loads of step s + 3.
-  auto mem_k = [&](Frags& nxt, const uint8_t* rb, uint8_t* lb, int s3, int k) {
-    if (k < 8) {
-      nxt.b[k >> 1][k & 1] = *reinterpret_cast<const u32x4*>(rb + mx::B_OFF + ((4 * wm + (k >> 1)) * 2 + (k & 1)) * 1024 + lane * 16);
-    } else if (k < 16) {
-      const int kk = k - 8;
-      nxt.a[kk >> 1][kk & 1] = *reinterpret_cast<const u32x4*>(rb + mx::A_OFF + ((4 * wn + (kk >> 1)) * 2 + (kk & 1)) * 1024 + lane * 16);
-    } else if (k == 16) {
-      nxt.sb0 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
-      nxt.sb1 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
-    } else if (k == 17) {
-      nxt.sa0 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
-      nxt.sa1 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
-    } else if (k < 28) {
-      issue_unit(s3, lb, k - 18);
-    }
-  };
-  // Iteration s: wait until step s+1 is in LDS (its own loads, then the
-  // barrier for everyone's), then run step s's 32 MFMAs with the reads of
-  // step s+1 and the refill of the stage step s-1 used (with step s+3)
-  // placed between them, fenced so the compiler keeps that order.
-  auto body_full = [&](int s, Frags& cur, Frags& nxt) {   // needs s + 3 < nsteps
-    // cur's LDS reads were issued an iteration ago; retire them here so the
-    // 20 reads below need no counter slot (lgkmcnt counts at most 15)
-    SVDQ_WAIT_LGKM0();
-    SVDQ_WAIT_VM(10);
-    __builtin_amdgcn_s_barrier();
-    const uint8_t* rb = smem + ((s + 1) & 3) * mx::STAGE_BYTES;
-    uint8_t* lb = smem + ((s + 3) & 3) * mx::STAGE_BYTES;
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      mfma_k(cur, k);
-      mem_k(nxt, rb, lb, s + 3, k);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  // the last K steps: wait for step s+1 (if it is a K step), refill, read,
-  // compute step s
-  auto body_tail = [&](int s, Frags& cur, Frags& nxt) {
-    SVDQ_WAIT_LGKM0();
-    if (s + 1 < nsteps) {
-      if (s + 2 < total) SVDQ_WAIT_VM(10);
-      else SVDQ_WAIT_VM(0);
-      __builtin_amdgcn_s_barrier();
-      if (s + 3 < total) issue(s + 3, (s + 3) & 3);
-      read_frags(nxt, (s + 1) & 3);
-    }
-    compute(cur);
-  };
-  static_assert(mx::STAGES == 4, "the step bookkeeping assumes a 4-stage ring");
+  f32x16 acc[4][4];
 
-  // bias of the workgroup's 256 columns, staged once (64 floats per wave)
-  float* bias_lds = reinterpret_cast<float*>(smem + mx::STAGES * mx::STAGE_BYTES);
   {
-    int64_t nb = n0 + 64 * wave + lane;
-    nb = nb < p.N ? nb : p.N - 1;
-    lds_load4(p.bias + nb, bias_lds + 64 * wave);
-  }
+    // XCD-aware tile index: workgroups are dealt to the 8 XCDs round robin,
+    // so give XCD x a contiguous range of the tile order (they share its L2)
+    const int T = p.tiles_n * p.tiles_m;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, kx = bid >> 3, per = T >> 3, rem = T & 7;
+    const int tile = xcd * per + (xcd < rem ? xcd : rem) + kx;
+    // grouped tile order: GROUP_M m-tiles sweep the n-tiles
+    const int gsz_full = mx::GROUP_M * p.tiles_n;
+    const int grp = tile / gsz_full, first_m = grp * mx::GROUP_M;
+    const int gm = (p.tiles_m - first_m) < mx::GROUP_M ? (p.tiles_m - first_m) : mx::GROUP_M;
+    const int within = tile - grp * gsz_full;
+    const int tm = first_m + within % gm, tn = within / gm;
+    const int64_t n0 = int64_t(tn) * 256, m0 = int64_t(tm) * 256;
+    // After the K steps come "low-rank steps": each stages two 16-rank chunks
+    // of L2 (weight side) and T (token side) through the same pipeline, and
+    // runs the up-projection on the 16-bit MFMA into the same accumulators.
+    const int nk = nsteps;
+    const int total = nk + (p.nchunks16 + 1) / 2;
+
+    int64_t tA[4], tB[4];
 #pragma unroll
-  for (int s = 0; s < mx::STAGES - 1; ++s)
-    if (s < total) issue(s, s);
-  if (total > 2) SVDQ_WAIT_VM(20);
-  else if (total > 1) SVDQ_WAIT_VM(10);
-  else SVDQ_WAIT_VM(0);
-  __builtin_amdgcn_s_barrier();
-  Frags F0, F1;
-  read_frags(F0, 0);
-  int s = 0;
-  for (; s + 4 < nsteps; s += 2) {       // steady state: every step issued is a K step
-    body_full(s, F0, F1);
-    body_full(s + 1, F1, F0);
-  }
-  for (; s < nsteps; s += 2) {
-    body_tail(s, F0, F1);
-    if (s + 1 < nsteps) body_tail(s + 1, F1, F0);
-  }
-  // low-rank steps (their loads were issued during the last K steps)
-  for (int q = nsteps; q < total; ++q) {
+    for (int f = 0; f < 4; ++f) {
+      const int u = 4 * wave + f;
+      const int64_t nt = n0 / 32 + u / 2;
+      tA[f] = nt < ntiles_n ? nt : ntiles_n - 1;   // a partial last tile re-reads a valid tile
+      tB[f] = m0 / 32 + u / 2;
+    }
+    int64_t pn = n0 / 64 + wave;
+    pn = pn < p.N / 64 ? pn : p.N / 64 - 1;
+    const uint8_t* gsa = p.sw + (pn * nsteps) * 256 + lane * 4;
+    const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
+    const uint8_t* l2b = reinterpret_cast<const uint8_t*>(p.l2) + lane * 16;
+    const uint8_t* ttb = reinterpret_cast<const uint8_t*>(p.t) + lane * 16;
+    // this wave's fixed source addresses; step r adds r * 2048 (fragments)
+    // or r * 256 (scales)
+    const uint8_t* ga[4];
+    const uint8_t* gb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int h = (4 * wave + f) & 1;
+      ga[f] = p.wq + (tA[f] * nsteps * 2 + h) * 1024 + lane * 16;
+      gb[f] = p.xq + (tB[f] * nsteps * 2 + h) * 1024 + lane * 16;
+    }
+    // one of the 10 loads a wave issues per K step
+    auto issue_unit = [&](int r, uint8_t* base, int x) {
+      if (x < 4) lds_load16(ga[x] + int64_t(r) * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
+      else if (x < 8) lds_load16(gb[x - 4] + int64_t(r) * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
+      else if (x == 8) lds_load4(gsa + int64_t(r) * 256, base + mx::SA_OFF + wave * 256);
+      else lds_load4(gsb + int64_t(r) * 256, base + mx::SB_OFF + wave * 256);
+    };
+    // the 10 loads of low-rank step e: chunks 2e, 2e+1 of L2 and T (the scale
+    // slots reload the first step's scales so every step issues 10 loads)
+    auto issue_lr = [&](int e, uint8_t* base) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int h = (4 * wave + f) & 1;
+        int c = 2 * e + h;
+        c = c < p.nchunks16 ? c : p.nchunks16 - 1;
+        lds_load16(l2b + (tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
+        lds_load16(ttb + (tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
+      }
+      lds_load4(gsa, base + mx::SA_OFF + wave * 256);
+      lds_load4(gsb, base + mx::SB_OFF + wave * 256);
+    };
+    auto issue = [&](int r, int st) {
+      uint8_t* base = smem + st * mx::STAGE_BYTES;
+      if (r < nk) {
+#pragma unroll
+        for (int x = 0; x < 10; ++x) issue_unit(r, base, x);
+      } else {
+        issue_lr(r - nk, base);
+      }
+    };
+    auto read_frags = [&](Frags& F, int st) {
+      const uint8_t* base = smem + st * mx::STAGE_BYTES;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          F.b[j][h] = *reinterpret_cast<const u32x4*>(base + mx::B_OFF + ((4 * wm + j) * 2 + h) * 1024 + lane * 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          F.a[i][h] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + ((4 * wn + i) * 2 + h) * 1024 + lane * 16);
+      F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
+      F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
+      F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
+      F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+    };
+    // One MFMA of a K step (k = 0..31 walks h, i, j; the two halves of a
+    // tile's K are 16 MFMAs apart, so no MFMA waits on its predecessor).
+    auto mfma_k = [&](const Frags& F, int k) {
+      const int h = k >> 4, i = (k >> 2) & 3, j = k & 3;
+      const i32x8 a = i32x8{int(F.a[i][h][0]), int(F.a[i][h][1]), int(F.a[i][h][2]), int(F.a[i][h][3]), 0, 0, 0, 0};
+      const i32x8 b = i32x8{int(F.b[j][h][0]), int(F.b[j][h][1]), int(F.b[j][h][2]), int(F.b[j][h][3]), 0, 0, 0, 0};
+      acc[i][j] = mfma_mx32(a, b, acc[i][j], i < 2 ? F.sa0 : F.sa1, j < 2 ? F.sb0 : F.sb1, 2 * (i & 1) + h, 2 * (j & 1) + h);
+    };
+    auto compute = [&](const Frags& F) {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) mfma_k(F, k);
+    };
+    // up-projection of low-rank step e: chunks 2e, 2e+1 of T L2
+    auto compute_lr = [&](int e, const Frags& F) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (2 * e + h < p.nchunks16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32x16<DT>(F.a[i][h], F.b[j][h], acc[i][j]);
+        }
+    };
+    // Memory op k of the next step, placed after MFMA k.  The 10 global->LDS
+    // loads of step r + 3 go after every third MFMA (k = 1, 4, ..., 28) so the
+    // four waves never queue more than the texture path drains per MFMA; the
+    // other slots take the 8 token and 8 weight fragment reads of step r + 1,
+    // then its 4 scale reads.
+    auto mem_k = [&](Frags& nxt, const uint8_t* rb, uint8_t* lb, int r3, int k) {
+      const int d = dma_slot(k);
+      if (d >= 0) {
+        issue_unit(r3, lb, d);
+        return;
+      }
+      const int e = lds_slot(k);
+      if (e < 8) {
+        nxt.b[e >> 1][e & 1] = *reinterpret_cast<const u32x4*>(rb + mx::B_OFF + ((4 * wm + (e >> 1)) * 2 + (e & 1)) * 1024 + lane * 16);
+      } else if (e < 16) {
+        const int ee = e - 8;
+        nxt.a[ee >> 1][ee & 1] = *reinterpret_cast<const u32x4*>(rb + mx::A_OFF + ((4 * wn + (ee >> 1)) * 2 + (ee & 1)) * 1024 + lane * 16);
+      } else if (e == 16) {
+        nxt.sb0 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
+        nxt.sb1 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
+      } else if (e == 17) {
+        nxt.sa0 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
+        nxt.sa1 = *reinterpret_cast<const int*>(rb + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+      }
+    };
+    // Iteration r: wait until step r+1 is in LDS (its own loads, then the
+    // barrier for everyone's), then run step r's 32 MFMAs with the reads of
+    // step r+1 and the refill of the stage step r-1 used (with step r+3)
+    // placed between them, fenced so the compiler keeps that order.
+    auto body_full = [&](int r, Frags& cur, Frags& nxt) {   // needs r + 3 < nk
+      // cur's LDS reads were issued an iteration ago; retire them here so the
+      // 20 reads below need no counter slot (lgkmcnt counts at most 15)
+      SVDQ_WAIT_LGKM0();
+      SVDQ_WAIT_VM(10);
+      __builtin_amdgcn_s_barrier();
+      const uint8_t* rb = smem + ((r + 1) & 3) * mx::STAGE_BYTES;
+      uint8_t* lb = smem + ((r + 3) & 3) * mx::STAGE_BYTES;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        mfma_k(cur, k);
+        mem_k(nxt, rb, lb, r + 3, k);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // the last K steps: wait for step r+1 (if it is a K step), refill, read,
+    // compute step r
+    auto body_tail = [&](int r, Frags& cur, Frags& nxt) {
+      SVDQ_WAIT_LGKM0();
+      if (r + 1 < nk) {
+        if (r + 2 < total) SVDQ_WAIT_VM(10);
+        else SVDQ_WAIT_VM(0);
+        __builtin_amdgcn_s_barrier();
+        if (r + 3 < total) issue(r + 3, (r + 3) & 3);
+        read_frags(nxt, (r + 1) & 3);
+      }
+      compute(cur);
+    };
+    static_assert(mx::STAGES == 4, "the step bookkeeping assumes a 4-stage ring");
+
+    // The bias of this wave's 128 columns, issued before the stage loads so
+    // the prologue's wait covers it.  Lane l < 32 takes column 32i + l.
+    float bcol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t nb = n0 + 128 * wn + 32 * i + (lane & 31);
+      nb = nb < p.N ? nb : p.N - 1;
+      bcol[i] = p.bias[nb];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < mx::STAGES - 1; ++r)
+      if (r < total) issue(r, r);
+    if (total > 2) SVDQ_WAIT_VM(20);
+    else if (total > 1) SVDQ_WAIT_VM(10);
+    else SVDQ_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
+    // Accumulators start at the bias: one 32 x 32 x 16 MFMA per tile with a
+    // zero C operand (no separate zero fill or bias add).  A holds the
+    // bias in k = 0..3 of lanes 0..31 (a 16-bit bias times 1.0 is exact), B of
+    // tile column j holds 1.0 at k = j only, so each product picks the bias
+    // once and the 16 MFMAs stay distinct.
+    {
+      const bool lo = lane < 32;
+      const unsigned one = lo ? (DT == SVDQ_BF16 ? 0x3F80u : 0x3C00u) : 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned bh = lo ? (pack2<DT>(bcol[i], 0.0f) & 0xFFFFu) : 0u;
+        const u32x4 ab = u32x4{bh | (bh << 16), bh | (bh << 16), 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 bj = u32x4{j == 0 ? one : j == 1 ? one << 16 : 0u, j == 2 ? one : j == 3 ? one << 16 : 0u, 0u, 0u};
+          acc[i][j] = mfma32x16<DT>(ab, bj, f32x16{});
+        }
+      }
+    }
+    Frags F0, F1;
+    read_frags(F0, 0);
+    int r = 0;
+    for (; r + 4 < nk; r += 2) {            // steady state: every step issued is a K step
+      body_full(r, F0, F1);
+      body_full(r + 1, F1, F0);
+    }
+    for (; r < nk; r += 2) {
+      body_tail(r, F0, F1);
+      if (r + 1 < nk) body_tail(r + 1, F1, F0);
+    }
+    // low-rank steps (their loads were issued during the last K steps)
+    for (int q = nk; q < total; ++q) {
+      SVDQ_WAIT_LGKM0();
+      SVDQ_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+      if (q + 3 < total) issue(q + 3, (q + 3) & 3);
+      Frags F;
+      read_frags(F, q & 3);
+      SVDQ_WAIT_LGKM0();
+      compute_lr(q - nk, F);
+    }
     SVDQ_WAIT_LGKM0();
     SVDQ_WAIT_VM(0);
-    __builtin_amdgcn_s_barrier();
-    if (q + 3 < total) issue(q + 3, (q + 3) & 3);
-    Frags F;
-    read_frags(F, q & 3);
-    SVDQ_WAIT_LGKM0();
-    compute_lr(q - nsteps, F);
-  }
 
-  // epilogue: bias, GELU, round; stage the wave's 128 x 128 tile in LDS as
-  // [token][column] rows, then store whole 256-byte row segments
-  SVDQ_WAIT_LGKM0();
-  SVDQ_WAIT_VM(0);
-  __syncthreads();                       // every wave is done with the LDS ring
-  uint8_t* ob = smem + wave * (128 * mx::OUT_PITCH);
-  const int64_t nw = n0 + 128 * wn;      // first column of this wave's tile
+    // ---- epilogue: (GELU,) round; stage the wave's 128 x 128 tile in LDS as
+    // [token][column] rows, then store whole 256-byte row segments
+    SVDQ_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();          // every wave is done with the LDS ring
+    uint8_t* ob = smem + wave * (128 * mx::OUT_PITCH);
+    const int64_t nw = n0 + 128 * wn;      // first column of this wave's tile
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      // accumulator v = 4g + r of tile (i, j): column 32i + 8g + 4(lane / 32) + r, token 32j + lane % 32
-      const int nl = 32 * i + 8 * g + 4 * (lane >> 5);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(bias_lds + 128 * wn + nl);
+      for (int gg = 0; gg < 4; ++gg) {
+        // accumulator 4gg + r of tile (i, j): column 32i + 8gg + 4(lane / 32) + r, token 32j + lane % 32
+        const int nl = 32 * i + 8 * gg + 4 * (lane >> 5);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v[4];
+        for (int j = 0; j < 4; ++j) {
+          float vv[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][4 * g + r] + bv[r];
-          if constexpr (GELU) v[r] = gelu_erf(v[r]);
+          for (int x = 0; x < 4; ++x) {
+            vv[x] = acc[i][j][4 * gg + x];
+            if constexpr (GELU) vv[x] = gelu_erf(vv[x]);
+          }
+          const int ml = 32 * j + (lane & 31);
+          *reinterpret_cast<u32x2*>(ob + ml * mx::OUT_PITCH + nl * 2) = u32x2{pack2<DT>(vv[0], vv[1]), pack2<DT>(vv[2], vv[3])};
         }
-        const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
-        const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
-        const int ml = 32 * j + (lane & 31);
-        *reinterpret_cast<u32x2*>(ob + ml * mx::OUT_PITCH + nl * 2) = u32x2{lo, hi};
       }
     }
-  }
-  SVDQ_WAIT_LGKM0();
-  if (nw < p.N) {
-    const int64_t mw = m0 + 128 * wm;
+    SVDQ_WAIT_LGKM0();
+    if (nw < p.N) {
+      const int64_t mw = m0 + 128 * wm;
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-      const int row = 4 * it + (lane >> 4);
-      const int col = (lane & 15) * 8;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
-      if (mw + row < p.M) *reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col) = v;
+      for (int it = 0; it < 32; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const int col = (lane & 15) * 8;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
+        if (mw + row < p.M) *reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col) = val;
+      }
     }
   }
 }
@@ -751,16 +821,16 @@ void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
 }
 
 template <int DT>
-void launch_k2_mx(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
+void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   MxParams mp;
   mp.wq = kp.wq; mp.sw = kp.sw; mp.l2 = kp.l2; mp.bias = kp.bias; mp.xq = kp.xq; mp.sx = kp.sx; mp.t = kp.t;
   mp.Y = kp.Y; mp.ldy = kp.ldy; mp.M = kp.M; mp.N = kp.N; mp.K = kp.K; mp.slots = kp.slots;
   mp.nchunks16 = kp.nchunks16;
   mp.tiles_n = int(svdq::ceil_div(kp.N, 256));
-  mp.tiles_m = int(Mp / 256);
-  dim3 grid(unsigned(mp.tiles_n * mp.tiles_m));
-  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), grid, dim3(256), 0, st, mp);
-  else hipLaunchKernelGGL((k2_mx<DT, false>), grid, dim3(256), 0, st, mp);
+  mp.tiles_m = int(w.Mp / 256);
+  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
+  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), dim3(T), dim3(256), 0, st, mp);
+  else hipLaunchKernelGGL((k2_mx<DT, false>), dim3(T), dim3(256), 0, st, mp);
 }
 
 svdq_status check_device_layer(const svdq_layer* L) {
@@ -835,8 +905,8 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
     else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
   } else {
-    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2_mx<SVDQ_F16>(kp, w.Mp, gelu, stream);
+    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w, gelu, stream);
+    else launch_k2_mx<SVDQ_F16>(kp, w, gelu, stream);
   }
   return launch_ok();
 }
