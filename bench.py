@@ -52,7 +52,46 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="distinct X/Y/weight buffer sets cycled per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the layer, time a plain device copy of MIB MiB (the reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k2_gemm_flux_fc1_mxfp4_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "diffusion_smooth_group_amd", "csrc", "svdq_kernels.hip")
+
+
+def measured_traffic(workload, fmt_name):
+    """HBM-side bytes per GEMM launch from the committed counter summary, or
+    None if there is none for this workload or the kernel source changed since."""
+    import hashlib
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if kv.get("kernel_source_sha256") != sha or kv.get("workload") != workload or kv.get("format") != fmt_name:
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of known size, for counter scaling."""
+    import torch
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 3}}), flush=True)
 
 
 def k1_bytes(M, K, r, fmt):
@@ -104,6 +143,9 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the layer's multi-GPU sharding "
               f"is a design note, not a run.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from diffusion_smooth_group_amd import svdq as S
     from diffusion_smooth_group_amd import workloads as wl
@@ -182,8 +224,17 @@ def main():
     wall = time.perf_counter() - tw0
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- per-kernel launch durations (HIP events on the launch stream)
+    # ---- per-kernel launch durations (HIP events on the launch stream): the
+    # mean over n back-to-back launches between two events, and the spread of
+    # n launches each bracketed by its own pair of events
     def per_launch(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mean = e0.elapsed_time(e1) * 1e3 / n
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
         for i in range(n):
             evs[i][0].record(stream)
@@ -191,7 +242,7 @@ def main():
             evs[i][1].record(stream)
         torch.cuda.synchronize()
         ts = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3   # us
-        return float(np.mean(ts)), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
+        return float(mean), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
 
     for i in range(nrot):       # workspaces hold this step's activations for k2-only timing
         k1(i)
@@ -222,7 +273,8 @@ def main():
                    "rotating_buffer_sets": nrot},
         "pct_of_peak": round(100.0 * tops / peak, 2),
         "roofline": {"bound": "mfma", "kernel": "k2_gemm", "achieved": round(k2_tflops, 1), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4),
+                     "traffic": measured_traffic(f"flux_{args.workload}_{M}x{K}x{N}", fmt_name),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": k2_bytes(M, K, N, args.rank, fmt_name)},
         "k1_roofline": {"bound": "hbm", "kernel": "k1_act", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
