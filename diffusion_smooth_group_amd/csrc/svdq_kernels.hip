@@ -85,6 +85,55 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt unconstrained
+#define SVDQ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
+// s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt unconstrained
+#define SVDQ_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4))
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* glb_ptr_t;
+
+__device__ __forceinline__ void lds_load16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+}
+
+// Max of a non-negative float over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
+// lanes q = 0..3 of one token in the activation kernel).  permlane16_swap
+// with both operands x leaves x of lanes l and l ^ 16 in its two results,
+// permlane32_swap likewise for l ^ 32; non-negative floats order as their
+// bit patterns.
+__device__ __forceinline__ unsigned umax_u(unsigned a, unsigned b) { return a > b ? a : b; }
+__device__ __forceinline__ float quad_max(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const unsigned m16 = umax_u(r16[0], r16[1]);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(m16, m16, false, false);
+  return __uint_as_float(umax_u(r32[0], r32[1]));
+}
+
+// e8m0 exponent of an MXFP4 block with absmax a: the biased exponent of
+// t = fl32(a / 6) plus one if t is not a power of two (so 2^(e-127) >= t),
+// 0 for t = 0, at most 254.  For a normal a = 1.f x 2^(B-127) with B >= 3,
+// a / 6 = (1.f / 1.5) 2^(B-129) never rounds across a power of two, and t is
+// itself a power of two only when 1.f = 1.5, so e = B - 2 + (f > 0.5)
+// exactly; tiny a (B < 3, t possibly subnormal) takes the division.
+__device__ __forceinline__ int e8m0_fast(float a) {      // exact for a >= 2^-124
+  const unsigned b = __float_as_uint(a);
+  const int B = int(b >> 23);                    // a >= 0: no sign bit
+  return B >= 255 ? 254 : B - 2 + ((b & 0x7FFFFFu) > 0x400000u ? 1 : 0);
+}
+__device__ __forceinline__ int e8m0_slow(float a) {      // any a >= 0
+  const float t = a / 6.0f;
+  const unsigned tb = __float_as_uint(t);
+  if (t == 0.0f) return 0;
+  const int e = int(tb >> 23) + ((tb & 0x7FFFFFu) != 0u ? 1 : 0);
+  return e > 254 ? 254 : e;
+}
+__device__ __forceinline__ bool e8m0_needs_slow(float a) { return (__float_as_uint(a) >> 23) < 3u; }
+
 // E2M1 magnitude index of a >= 0: nearest value, ties to the even mantissa, saturating at 6.
 __device__ __forceinline__ unsigned e2m1_index(float a) {
   return unsigned(a > 0.25f) + unsigned(a >= 0.75f) + unsigned(a > 1.25f) + unsigned(a >= 1.75f) +
@@ -103,129 +152,239 @@ struct K1Params {
   uint16_t* t;
 };
 
-// One workgroup = 16 tokens; its 4 waves take the 128-deep K steps round robin.
-// Lane l holds token (l % 16) and k in [32q, 32q+32) of a step (q = l / 16).
-template <int FMT, int DT>
-__global__ __launch_bounds__(256) void k1_act(K1Params p) {
+// One workgroup = 16 tokens; its 4 waves take the 128-deep K steps round
+// robin.  Lane l = m + 16q holds token m and, in chunk c = 0..3 of a step,
+// k in [32c + 8q, 32c + 8q + 8): the four lanes of a token read 64
+// contiguous bytes per load instruction.  An MXFP4 block (32 k) is chunk c
+// of lanes q = 0..3; an INT4 64-group is chunks 2g and 2g + 1 of those lanes.
+//
+// Latency.  The vector memory counter retires in issue order, so waiting for
+// a short (L2) load also waits for every older HBM load.  A wave therefore
+// works in chunks of K1Chunk steps: it issues the X of the whole chunk at
+// once, quantizes the steps as they arrive (in order), and only then runs
+// the chunk's down-projection from the X still in registers, with the L1x
+// fragments -- the only loads in flight by then -- streamed two steps
+// ahead.  Every memory operation is unconditional (indices past the wave's
+// last step are clamped, so padding steps rewrite identical codes and add
+// zero to T), which keeps the compiler's counter bookkeeping exact.
+// invlambda is copied to LDS by direct global->LDS loads before anything
+// else, when it fits.
+constexpr int K1_IL_LDS_MAX_K = 16384;
+template <int NJT> struct K1Chunk { static constexpr int value = NJT <= 2 ? 6 : (NJT <= 4 ? 3 : 2); };
+template <int NJT> struct K1LRing { static constexpr int value = NJT <= 4 ? 2 : 1; };
+
+template <int FMT, int DT, int NJT, bool IL_LDS>
+__global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves per SIMD at least
+  // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction buffer
+  extern __shared__ __attribute__((aligned(16))) uint8_t k1_lds[];
+  constexpr int CH = K1Chunk<NJT>::value;
+  constexpr int LR = K1LRing<NJT>::value;
   const int mt = blockIdx.x;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int64_t row = int64_t(mt) * 16 + m;
   const bool valid = row < p.M;
   const int nsteps = int(p.K / KSTEP);
-  const uint16_t* xrow = p.X + (valid ? row : 0) * p.ldx;
+  const int nmine = (nsteps - wave + 3) / 4;     // this wave's steps: wave, wave + 4, ...
+  const uint16_t* xrow = p.X + (valid ? row : 0) * p.ldx + 8 * q;
+  const float* il_lds = reinterpret_cast<const float*>(k1_lds);
+  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + (IL_LDS ? size_t(p.K) * 4 : 0));   // [4][NJT][64]
 
-  f32x4 tacc[MAXJT];
-#pragma unroll
-  for (int j = 0; j < MAXJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (IL_LDS) {
+    // wave w copies 1 KB pieces w, w + 4, ... of invlambda
+    for (int c = wave; c * 256 < p.K; c += 4)
+      lds_load16(p.invlam + c * 256 + lane * 4, k1_lds + c * 1024);
+  }
 
-  for (int s = wave; s < nsteps; s += 4) {
-    const int k0 = s * KSTEP + q * 32;
-    u32x4 xr[4];
+  f32x4 tacc[NJT > 0 ? NJT : 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      xr[i] = valid ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < NJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int njc = p.njt > 0 ? p.njt - 1 : 0;
+  auto step_of = [&](int i) { return wave + 4 * (i < nmine ? i : nmine - 1); };
+  u32x4 xr[CH][4];
+  u32x4 lring[LR][NJT > 0 ? NJT : 1][4];
+  auto load_x = [&](int slot, int i) {
+    const int s = step_of(i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      xr[slot][c] = valid ? *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto load_l1x = [&](int slot, int i) {
+    const int s = step_of(i);
+    const u32x4* l1 = reinterpret_cast<const u32x4*>(p.l1x) + (size_t(s) * (p.slots / 16)) * 4 * 64 + lane;
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) lring[slot][jt][c] = l1[((jt < njc ? jt : njc) * 4 + c) * 64];
+  };
+
+  // quantize one step: codes and scales of 16 tokens x 128 k
+  auto quantize = [&](const u32x4 (&xq)[4], int s) {
+    // smoothed values x_hat = x * invlambda (one fp32 multiply)
+    float xh[4][8];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = s * KSTEP + 32 * c + 8 * q;
+      f32x4 il0, il1;
+      if constexpr (IL_LDS) {
+        il0 = *reinterpret_cast<const f32x4*>(il_lds + k);
+        il1 = *reinterpret_cast<const f32x4*>(il_lds + k + 4);
+      } else {
+        il0 = *reinterpret_cast<const f32x4*>(p.invlam + k);
+        il1 = *reinterpret_cast<const f32x4*>(p.invlam + k + 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned w = xq[c][e];
+        const f32x4& il = e < 2 ? il0 : il1;
+        xh[c][2 * e] = h2f<DT>(w & 0xFFFFu) * il[(2 * e) & 3];
+        xh[c][2 * e + 1] = h2f<DT>(w >> 16) * il[(2 * e + 1) & 3];
+      }
     }
-    float xh[32];
+    float am[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 il = *reinterpret_cast<const f32x4*>(p.invlam + k0 + 4 * i);
-      const unsigned w0 = xr[i >> 1][(i & 1) * 2], w1 = xr[i >> 1][(i & 1) * 2 + 1];
-      xh[4 * i + 0] = h2f<DT>(w0 & 0xFFFFu) * il[0];
-      xh[4 * i + 1] = h2f<DT>(w0 >> 16) * il[1];
-      xh[4 * i + 2] = h2f<DT>(w1 & 0xFFFFu) * il[2];
-      xh[4 * i + 3] = h2f<DT>(w1 >> 16) * il[3];
+    for (int c = 0; c < 4; ++c) {
+      am[c] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am[c] = fmaxf(am[c], fabsf(xh[c][e]));
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(xh[i]));
 
     if constexpr (FMT == SVDQ_FMT_INT4_G64) {
+      unsigned d[4];
+      unsigned sh[2];
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const float a = quad_max(fmaxf(am[2 * g], am[2 * g + 1]));
+        const float sc = fminf(a / 7.0f, 65504.0f);
+        sh[g] = f2h<SVDQ_F16>(sc);
+        const float s32 = h2f<SVDQ_F16>(sh[g]);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const int c = 2 * g + cc;
+          unsigned v = 0u;
+          if (s32 != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              float r = rintf(xh[c][e] / s32);
+              r = fminf(fmaxf(r, -7.0f), 7.0f);
+              v |= (unsigned(int(r)) & 0xFu) << (4 * e);
+            }
+          }
+          d[c] = v;
+        }
+      }
       uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
-      amax = fmaxf(amax, __shfl_xor(amax, 16));            // the 64-group spans lanes q and q^1
-      float sc = fminf(amax / 7.0f, 65504.0f);
-      const unsigned sh = f2h<SVDQ_F16>(sc);
-      const float s32 = h2f<SVDQ_F16>(sh);
-      unsigned d[4] = {0u, 0u, 0u, 0u};
-      if (s32 != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          float r = rintf(xh[i] / s32);
-          r = fminf(fmaxf(r, -7.0f), 7.0f);
-          const unsigned c = unsigned(int(r)) & 0xFu;
-          d[i >> 3] |= c << (4 * (i & 7));
-        }
-      }
-      // k in [32q, 32q+16) -> slot (m, 2(q%2)), k in [32q+16, 32q+32) -> slot (m, 2(q%2)+1);
-      // byte half = 64-group within the step (q / 2)
-      const int qa = 2 * (q & 1), half = 8 * (q >> 1);
-      *reinterpret_cast<u32x2*>(frag + (m + 16 * qa) * 16 + half) = u32x2{d[0], d[1]};
-      *reinterpret_cast<u32x2*>(frag + (m + 16 * (qa + 1)) * 16 + half) = u32x2{d[2], d[3]};
-      if ((q & 1) == 0) {
-        uint16_t* sxp = reinterpret_cast<uint16_t*>(p.sx);
-        sxp[((size_t(mt) * nsteps + s) * 16 + m) * 2 + (q >> 1)] = (uint16_t)sh;
-      }
+      *reinterpret_cast<u32x4*>(frag + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
+      if (q == 0)
+        reinterpret_cast<unsigned*>(p.sx)[(size_t(mt) * nsteps + s) * 16 + m] = sh[0] | (sh[1] << 16);
     } else {
-      const float tq = amax / 6.0f;
-      const unsigned tb = __float_as_uint(tq);
-      int e = int((tb >> 23) & 0xFFu) + ((tb & 0x7FFFFFu) != 0u ? 1 : 0);
-      if (tq == 0.0f) e = 0;
-      e = e > 254 ? 254 : e;
-      unsigned d[4] = {0u, 0u, 0u, 0u};
+      // block maxima across the four lanes of a token, all blocks at once
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float u = ldexpf(xh[i], 127 - e);
-        const unsigned c = e2m1_index(fabsf(u)) | ((__float_as_uint(xh[i]) >> 28) & 8u);
-        d[i >> 3] |= c << (4 * (i & 7));
+      for (int c = 0; c < 4; ++c) am[c] = quad_max(am[c]);
+      int ex[4];
+      bool slow = false;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ex[c] = e8m0_fast(am[c]);
+        slow |= e8m0_needs_slow(am[c]);
       }
-      // 32-row fragment tile t32 = mt / 2; K block q of the step -> half q / 2,
-      // lane (row in the 32-tile) + 32 (q % 2)
-      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
-      const int l32 = r32 + 32 * (q & 1), h = q >> 1;
-      uint8_t* frag32 = p.xq + ((size_t(t32) * nsteps + s) * 2 + h) * 1024;
-      *reinterpret_cast<u32x4*>(frag32 + l32 * 16) = u32x4{d[0], d[1], d[2], d[3]};
-      // scale byte 2 (t32 % 2) + h of the dword of the 32-tile pair (op_sel in the GEMM)
-      p.sx[((size_t(t32 >> 1) * nsteps + s) * 64 + l32) * 4 + 2 * (t32 & 1) + h] = (uint8_t)e;
-    }
-
-    // down-projection T^T += L1x^T X^T on the raw 16-bit inputs
-    const u32x4* l1 = reinterpret_cast<const u32x4*>(p.l1x) + (size_t(s) * (p.slots / 16)) * 4 * 64;
+      if (__builtin_expect(slow, 0)) {
 #pragma unroll
-    for (int jt = 0; jt < MAXJT; ++jt) {
-      if (jt < p.njt) {
+        for (int c = 0; c < 4; ++c)
+          if (e8m0_needs_slow(am[c])) ex[c] = e8m0_slow(am[c]);
+      }
+      unsigned d[4];
 #pragma unroll
-        for (int jp = 0; jp < 4; ++jp) {
-          const u32x4 a = l1[(jt * 4 + jp) * 64 + lane];
-          tacc[jt] = mfma16<DT>(a, xr[jp], tacc[jt]);
+      for (int c = 0; c < 4; ++c) {
+        // The packed fp32 -> E2M1 conversion divides by the power-of-two
+        // scale 2^(e-127) (exact) and rounds to the nearest E2M1 value, ties
+        // to the even mantissa, saturating at 6, keeping the sign of zero --
+        // the group quantizer's rule.  An all-zero block (e = 0) uses scale 1.
+        const int e = ex[c];
+        const float scl = e != 0 ? __uint_as_float(unsigned(e) << 23) : 1.0f;
+        unsigned v = 0u;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const unsigned cv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xh[c][2 * b], xh[c][2 * b + 1], scl, 0);
+          v |= (cv & 0xFFu) << (8 * b);
         }
+        d[c] = v;
       }
+      // 32-row fragment tile t32 = mt / 2; block c of the step -> half c / 2,
+      // lane (row in the 32-tile) + 32 (c % 2), bytes [4q, 4q + 4)
+      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint8_t* frag32 = p.xq + ((size_t(t32) * nsteps + s) * 2 + (c >> 1)) * 1024;
+        *reinterpret_cast<unsigned*>(frag32 + (r32 + 32 * (c & 1)) * 16 + 4 * q) = d[c];
+      }
+      // scale bytes 2 (t32 % 2) + h of the dword of lane (row + 32 (c % 2)):
+      // blocks (0, 2) and (1, 3) share a dword; lanes q = 0 and 1 write one each
+      if (q < 2) {
+        uint16_t* sxp = reinterpret_cast<uint16_t*>(p.sx + ((size_t(t32 >> 1) * nsteps + s) * 64 + r32 + 32 * q) * 4 + 2 * (t32 & 1));
+        *sxp = uint16_t(unsigned(ex[q]) | (unsigned(ex[q + 2]) << 8));
+      }
+    }
+  };
+
+  for (int i0 = 0; i0 < nmine; i0 += CH) {
+    // the chunk's first L1x fragments, then all of its X
+#pragma unroll
+    for (int r = 0; r < LR; ++r) load_l1x(r, i0 + r);
+#pragma unroll
+    for (int d = 0; d < CH; ++d) load_x(d, i0 + d);
+    if constexpr (IL_LDS) {
+      if (i0 == 0) {
+        // the LDS copy of invlambda is complete once only the loads issued
+        // after it are outstanding; every wave's piece is visible after the barrier
+        SVDQ_WAIT_VM(LR * 4 * NJT + 4 * CH);
+        __builtin_amdgcn_s_barrier();
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < CH; ++d) quantize(xr[d], step_of(i0 + d));
+    // down-projection T^T += L1x^T X^T on the raw 16-bit inputs (padding
+    // steps past the wave's last contribute zero)
+#pragma unroll
+    for (int d = 0; d < CH; ++d) {
+      const bool real = i0 + d < nmine;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4 a = lring[d % LR][jt][c];
+          tacc[jt] = mfma16<DT>(real ? a : u32x4{0u, 0u, 0u, 0u}, xr[d][c], tacc[jt]);
+        }
+      if (d + LR < CH) load_l1x(d % LR, i0 + d + LR);
     }
   }
 
-  if (p.njt == 0) return;
-  __shared__ f32x4 red[4][MAXJT][64];
+  if constexpr (NJT > 0) {
+    // T = the four waves' partial sums (fixed order), rounded once to 16 bits
+    if (p.njt == 0) return;
 #pragma unroll
-  for (int jt = 0; jt < MAXJT; ++jt)
-    if (jt < p.njt) red[wave][jt][lane] = tacc[jt];
-  __syncthreads();
-  for (int jt = wave; jt < p.njt; jt += 4) {
-    f32x4 v = red[0][jt][lane];
+    for (int jt = 0; jt < NJT; ++jt) red[(wave * NJT + jt) * 64 + lane] = tacc[jt];
+    __syncthreads();
+    for (int jt = wave; jt < p.njt; jt += 4) {
+      f32x4 v = red[jt * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) v += red[w][jt][lane];
-    // lane holds T[m][16 jt + 4q + i]; place it in the epilogue's B-fragment order
-    const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
-    const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
-    uint16_t* dst;
-    if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
-      // 32-row tiles, 16-rank chunks: lane (row in tile) + 32 (j % 16 >= 8)
-      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
-      dst = p.t + ((size_t(t32) * (p.slots / 16) + jt) * 64 + r32 + 32 * (q >> 1)) * 8 + 4 * (q & 1);
-    } else {
-      // 16-row tiles, 32-rank chunks
-      const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
-      dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
+      for (int w = 1; w < 4; ++w) v += red[(w * NJT + jt) * 64 + lane];
+      // lane holds T[m][16 jt + 4q + i]; place it in the epilogue's B-fragment order
+      const unsigned lo = pack2<DT>(v[0], v[1]);
+      const unsigned hi = pack2<DT>(v[2], v[3]);
+      uint16_t* dst;
+      if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
+        // 32-row tiles, 16-rank chunks: lane (row in tile) + 32 (j % 16 >= 8)
+        const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+        dst = p.t + ((size_t(t32) * (p.slots / 16) + jt) * 64 + r32 + 32 * (q >> 1)) * 8 + 4 * (q & 1);
+      } else {
+        // 16-row tiles, 32-rank chunks
+        const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
+        dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
+      }
+      *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
     }
-    *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
   }
 }
 
@@ -454,20 +613,7 @@ __device__ __forceinline__ f32x16 mfma32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* glb_ptr_t;
 
-__device__ __forceinline__ void lds_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt unconstrained
-#define SVDQ_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | ((((n) >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8))
-// s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt unconstrained
-#define SVDQ_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4))
 
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
@@ -811,7 +957,23 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 template <int FMT, int DT>
 void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
-  hipLaunchKernelGGL((k1_act<FMT, DT>), dim3(unsigned(Mp / 16)), dim3(256), 0, st, kp);
+  const dim3 grid(unsigned(Mp / 16)), block(256);
+  const bool il = kp.K <= K1_IL_LDS_MAX_K;
+  const size_t il_bytes = il ? size_t(kp.K) * 4 : 0;
+  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
+  if (kp.njt == 0) {
+    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 0, true>), grid, block, il_bytes, st, kp);
+    else hipLaunchKernelGGL((k1_act<FMT, DT, 0, false>), grid, block, 0, st, kp);
+  } else if (kp.njt <= 2) {
+    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 2, true>), grid, block, il_bytes + red_bytes(2), st, kp);
+    else hipLaunchKernelGGL((k1_act<FMT, DT, 2, false>), grid, block, red_bytes(2), st, kp);
+  } else if (kp.njt <= 4) {
+    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 4, true>), grid, block, il_bytes + red_bytes(4), st, kp);
+    else hipLaunchKernelGGL((k1_act<FMT, DT, 4, false>), grid, block, red_bytes(4), st, kp);
+  } else {
+    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, true>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
+    else hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, false>), grid, block, red_bytes(MAXJT), st, kp);
+  }
 }
 
 template <int DT>

@@ -10,9 +10,12 @@
 //          and the 32 E2M1 codes of k in [64h + 32(l / 32), +32) of the step
 //          (element 2i in the low nibble of byte i) -- one e8m0 block.
 //   INT4 (16 x 16 x 64 integer MFMA): per 16-row tile and step, 64 lanes x
-//          16 bytes; lane l holds row l % 16, bytes [0, 8) are k in
-//          [16q, 16q+16) (first 64-group), bytes [8, 16) are k in
-//          [64+16q, 64+16q+16) (second 64-group), q = l / 16.
+//          16 bytes; lane l holds row l % 16 and, in bytes [4c, 4c+4), the
+//          8 codes of k in [32c + 8q, 32c + 8q + 8), q = l / 16: bytes
+//          [0, 8) belong to the step's first 64-group, [8, 16) to the
+//          second.  (The order of k inside a group is free for an integer
+//          dot product; this one lets the activation kernel write each
+//          lane's 16 bytes straight from coalesced loads of X.)
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -97,10 +100,10 @@ inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int
     *byte = size_t(((t * nsteps + s) * 2 + h) * 1024 + lane * 16 + c / 2);
     *nib = int(c % 2);
   } else {
-    int64_t t = r / 16, g = kk / 64, w = kk % 64, q = w / 16, c = w % 16;
+    int64_t t = r / 16, c = kk / 32, q = (kk % 32) / 8, e = kk % 8;
     int64_t lane = (r % 16) + 16 * q;
-    *byte = size_t(((t * nsteps + s) * 64 + lane) * 16 + 8 * g + c / 2);
-    *nib = int(c % 2);
+    *byte = size_t(((t * nsteps + s) * 64 + lane) * 16 + 4 * c + e / 2);
+    *nib = int(e % 2);
   }
 }
 
@@ -146,12 +149,14 @@ inline size_t lr_pos(int64_t r, int64_t j, int slots, int fmt) {
 }
 
 // 16-bit L1x as the activation kernel reads it: (k, rank j).
-// Per (128-step, 16-rank tile, 32-K sub-step j'): 64 lanes x 8; lane covers
-// rank (j % 16) and k in [32q + 8j', 32q + 8j' + 8) of the step.
+// Per (128-step, 16-rank tile, 32-K block c): 64 lanes x 8; lane covers
+// rank (j % 16) and k in [32c + 8q, 32c + 8q + 8) of the step, q = lane / 16
+// (the A operand of a 16 x 16 x 32 MFMA whose B operand is the same lane's
+// slice of X).
 inline size_t l1x_pos(int64_t k, int64_t j, int slots) {
-  int64_t s = k / KSTEP, kk = k % KSTEP, q = kk / 32, w = kk % 32, jp = w / 8, e = w % 8, jt = j / 16;
+  int64_t s = k / KSTEP, kk = k % KSTEP, c = kk / 32, q = (kk % 32) / 8, e = kk % 8, jt = j / 16;
   int64_t lane = (j % 16) + 16 * q;
-  return size_t((((s * (slots / 16) + jt) * 4 + jp) * 64 + lane) * 8 + e);
+  return size_t((((s * (slots / 16) + jt) * 4 + c) * 64 + lane) * 8 + e);
 }
 
 }  // namespace svdq
