@@ -435,10 +435,16 @@ __device__ __forceinline__ float gelu_erf(float x) {
 }
 
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
-// 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).
+// 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per 64-group the
+// integer MFMA gives the exact partial P_g (the nibbles are widened to
+// 16 q per byte, so the MFMA sums 256 P_g); it is dequantized on the VALU
+// into fp32 accumulators: acc += f32(P) * (s_w * s_x / 256).  That dequant
+// bounds the kernel, so the accumulators live in VGPRs, each step's operands
+// and scales are loaded one step ahead, and two waves share a SIMD (one's
+// MFMAs run under the other's VALU work).
 template <int DT, bool GELU>
-__global__ __launch_bounds__(256) void k2_int4(K2Params p) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
@@ -446,61 +452,82 @@ __global__ __launch_bounds__(256) void k2_int4(K2Params p) {
   const int64_t nt0 = n0 / 16, mt0 = m0 / 16;
   const int nsteps = int(p.K / KSTEP);
 
+  const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq);
+  const u32x4* xq = reinterpret_cast<const u32x4*>(p.xq);
+  const uint16_t* sw16 = reinterpret_cast<const uint16_t*>(p.sw);
+  const uint16_t* sx16 = reinterpret_cast<const uint16_t*>(p.sx);
+
+  // one step's raw operands: 4 weight and 4 token fragments (both 64-groups),
+  // the weight scales of 4 x 4 columns x 2 groups, the token scales (2 groups)
+  struct Ops {
+    u32x4 a[4], b[4], sw[4];
+    unsigned sx[4];
+  };
+  auto load = [&](Ops& o, int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.a[i] = wq[((nt0 + i) * nsteps + s) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.b[j] = xq[((mt0 + j) * nsteps + s) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o.sw[i] = *reinterpret_cast<const u32x4*>(sw16 + ((((nt0 + i) * nsteps + s) * 4 + q) * 2) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o.sx[j] = *reinterpret_cast<const unsigned*>(sx16 + (((mt0 + j) * nsteps + s) * 16 + (lane & 15)) * 2);
+  };
+
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq);
-  const u32x4* xq = reinterpret_cast<const u32x4*>(p.xq);
-
-  for (int s = 0; s < nsteps; ++s) {
-    u32x4 a[4], b[4];
+  auto compute = [&](const Ops& o) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = wq[((nt0 + i) * nsteps + s) * 64 + lane];
+    for (int g = 0; g < 2; ++g) {
+      float sxf[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = xq[((mt0 + j) * nsteps + s) * 64 + lane];
-    {
-      // scales: weight side 4 consecutive n x 2 groups per lane, token side 2 groups per lane
-      const uint16_t* sw16 = reinterpret_cast<const uint16_t*>(p.sw);
-      const uint16_t* sx16 = reinterpret_cast<const uint16_t*>(p.sx);
-      float swf[4][2][4], sxf[4][2];
+      for (int j = 0; j < 4; ++j) sxf[j] = h2f<SVDQ_F16>((o.sx[j] >> (16 * g)) & 0xFFFFu) * (1.0f / 256.0f);
+      i32x4 ub[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(sw16 + ((((nt0 + i) * nsteps + s) * 4 + q) * 2) * 4);
+        // weight scales of this lane's 4 columns 16i + 4q + r in group g
+        float swf[4];
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int r = 0; r < 4; ++r) swf[r] = h2f<SVDQ_F16>((o.sw[i][g * 2 + (r >> 1)] >> (16 * (r & 1))) & 0xFFFFu);
+        const i32x4 ua = widen_nibbles(o.a[i][2 * g], o.a[i][2 * g + 1]);
+        // the row's four MFMAs first, so each dequant finds its product done
+        i32x4 P[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) swf[i][g][r] = h2f<SVDQ_F16>((v[g * 2 + (r >> 1)] >> (16 * (r & 1))) & 0xFFFFu);
-      }
+        for (int j = 0; j < 4; ++j) P[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned v = *reinterpret_cast<const unsigned*>(sx16 + (((mt0 + j) * nsteps + s) * 16 + (lane & 15)) * 2);
-        sxf[j][0] = h2f<SVDQ_F16>(v & 0xFFFFu) * (1.0f / 256.0f);
-        sxf[j][1] = h2f<SVDQ_F16>(v >> 16) * (1.0f / 256.0f);
-      }
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        i32x4 ua[4], ub[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ua[i] = widen_nibbles(a[i][2 * g], a[i][2 * g + 1]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) ub[j] = widen_nibbles(b[j][2 * g], b[j][2 * g + 1]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const i32x4 P = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[i], ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[i][j][r] = fmaf(float(P[r]), swf[i][g][r] * sxf[j][g], acc[i][j][r]);
-          }
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(float(P[j][r]), swf[r] * sxf[j], acc[i][j][r]);
       }
     }
-  }
+  };
 
-  // epilogue: + T L2 (16-bit MFMA into the same accumulators), + bias, GELU, round, store
+  // two-step software pipeline: step s + 1's loads are in flight while step
+  // s computes (the last step reloads itself, so every trip is the same)
+  Ops o0, o1;
+  load(o0, 0);
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    load(o1, s + 1);
+    compute(o0);
+    load(o0, s + 2 < nsteps ? s + 2 : nsteps - 1);
+    compute(o1);
+  }
+  if (s < nsteps) compute(o0);
+
+  // epilogue: + T L2 (16-bit MFMA into a separate accumulator, added on the
+  // VALU so the dequant accumulators stay in VGPRs), + bias, GELU, round, store
+  f32x4 lr[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lr[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4* l2 = reinterpret_cast<const u32x4*>(p.l2);
   const u32x4* tt = reinterpret_cast<const u32x4*>(p.t);
   for (int c = 0; c < p.nchunks; ++c) {
@@ -512,7 +539,7 @@ __global__ __launch_bounds__(256) void k2_int4(K2Params p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16<DT>(la[i], tb[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) lr[i][j] = mfma16<DT>(la[i], tb[j], lr[i][j]);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -525,12 +552,10 @@ __global__ __launch_bounds__(256) void k2_int4(K2Params p) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = acc[i][j][r] + bv[r];
+          v[r] = (acc[i][j][r] + lr[i][j][r]) + bv[r];
           if constexpr (GELU) v[r] = gelu_erf(v[r]);
         }
-        const unsigned lo = f2h<DT>(v[0]) | (f2h<DT>(v[1]) << 16);
-        const unsigned hi = f2h<DT>(v[2]) | (f2h<DT>(v[3]) << 16);
-        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{lo, hi};
+        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
       }
     }
   }
