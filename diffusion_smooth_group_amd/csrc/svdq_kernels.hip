@@ -188,7 +188,8 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   const int nmine = (nsteps - wave + 3) / 4;     // this wave's steps: wave, wave + 4, ...
   const uint16_t* xrow = p.X + (valid ? row : 0) * p.ldx + 8 * q;
   const float* il_lds = reinterpret_cast<const float*>(k1_lds);
-  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + (IL_LDS ? size_t(p.K) * 4 : 0));   // [4][NJT][64]
+  // invlambda is copied in whole 1 KB pieces, so its LDS copy spans K rounded up to 256
+  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + (IL_LDS ? size_t((p.K + 255) & ~int64_t(255)) * 4 : 0));   // [4][NJT][64]
 
   if constexpr (IL_LDS) {
     // wave w copies 1 KB pieces w, w + 4, ... of invlambda
@@ -357,6 +358,14 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
           tacc[jt] = mfma16<DT>(real ? a : u32x4{0u, 0u, 0u, 0u}, xr[d][c], tacc[jt]);
         }
       if (d + LR < CH) load_l1x(d % LR, i0 + d + LR);
+    }
+  }
+  if constexpr (IL_LDS) {
+    // a wave without K steps (K < 512) still meets the first chunk's barrier,
+    // so the T reduction's barrier pairs up across all four waves
+    if (nmine <= 0) {
+      SVDQ_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
     }
   }
 
@@ -984,7 +993,7 @@ template <int FMT, int DT>
 void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
   const bool il = kp.K <= K1_IL_LDS_MAX_K;
-  const size_t il_bytes = il ? size_t(kp.K) * 4 : 0;
+  const size_t il_bytes = il ? size_t((kp.K + 255) & ~int64_t(255)) * 4 : 0;
   auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
   if (kp.njt == 0) {
     if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 0, true>), grid, block, il_bytes, st, kp);

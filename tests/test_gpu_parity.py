@@ -36,6 +36,21 @@ def test_lora_gelu_and_ragged(fmt):
     G.run_layer_case(d, fmt, 32, lora=True, gelu=True, alpha=0.5)
 
 
+def test_mxfp4_many_tiles_full_parity():
+    # 4096 x 4096 outputs = 256 GEMM tiles of 256 x 256 (one per CU), every output checked
+    d = _small(4096, 256, 4096, o.BF16, o.MXFP4, 16, lora=16, seed=30)
+    G.run_layer_case(d, o.MXFP4, 16, lora=True, gelu=True)
+
+
+@pytest.mark.parametrize("K", [128, 256, 384])
+@pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
+def test_short_k_wide_low_rank(fmt, K):
+    # fewer 128-deep K steps than the activation kernel has waves, with a
+    # rank-48 branch (rank 16 + LoRA 32) whose T tiles every wave finalizes
+    d = _small(48, K, 256, o.BF16, fmt, 16, lora=32, seed=20 + K)
+    G.run_layer_case(d, fmt, 16, lora=True)
+
+
 @pytest.mark.parametrize("M", [1, 17, 256, 300])
 def test_token_counts(M):
     d = _small(M, 256, 128, o.F16, o.INT4, 8, seed=3 + M)
