@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="distinct X/Y/weight buffer sets cycled per step")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--kernel-iters", type=int, default=50)
+    ap.add_argument("--lowrank-study", action="store_true",
+                    help="instead of the headline line, time the forward three ways -- W4A4 only (rank 0), "
+                         "fused low-rank branch, low-rank branch as separate passes -- and print their overheads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, time a plain device copy of MIB MiB (the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -137,6 +140,84 @@ def cpu_baseline(spec, d, lin_export, fmt_name, rank):
                       f"{t * 1e3:.1f} ms each; host os.cpu_count()={os.cpu_count()}"}
 
 
+def lowrank_study(args):
+    """Cost of the low-rank branch on top of the 4-bit path: the layer with
+    its branch switched off (W4A4 only, same 4-bit codes), the fused forward,
+    and the branch run as separate passes (a second read of X, Y read back
+    and rewritten)."""
+    import ctypes as C
+    import torch
+    from diffusion_smooth_group_amd import svdq as S
+    from diffusion_smooth_group_amd import workloads as wl
+    fmt_name = "mxfp4_g32" if args.fmt == "mxfp4" else "int4_g64"
+    fmt = S.FMT_MXFP4_G32 if args.fmt == "mxfp4" else S.FMT_INT4_G64
+    M, K, N, dts = WORKLOADS[args.workload]
+    dt = S.BF16 if dts == "bf16" else S.F16
+    spec = {"fc1": wl.config_shapes(3)[0], "fc2": wl.config_shapes(3)[1]}.get(args.workload, wl.config_shapes(2)[0])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = wl.generate(spec)
+    Xd0 = S.bits_to_device(d["X"], dt, dev)
+    absmax = S.activation_absmax(Xd0, dt)
+    torch.cuda.synchronize()
+    am = absmax.cpu().numpy()
+    lin = S.SVDQLinear.pack(d["W"], dt, am, args.rank, fmt, d["bias"], rank_capacity=args.rank)
+    nrot = max(1, args.rotate)
+    lib = S.lib_handle()
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+    Xs = [Xd0] + [Xd0.clone() for _ in range(nrot - 1)]
+    Ys = [torch.empty((M, N), dtype=Xd0.dtype, device=dev) for _ in range(nrot)]
+    layers, blobs = [lin.layer], [lin.blob]
+    for _ in range(nrot - 1):
+        b = torch.empty_like(lin.blob)
+        layers.append(S.layer_copy(lin.layer, S._t_ptr(b), b.numel(), True))
+        blobs.append(b)
+    # W4A4 only: the same blobs (same 4-bit codes) with the low-rank branch
+    # switched off in the descriptor
+    plain = []
+    for L in layers:
+        L0 = S.svdq_layer.from_buffer_copy(L)
+        L0.rank = 0
+        L0.rank_active = 0
+        plain.append(L0)
+    wsb = S.workspace_size(lin.layer, M)
+    wss = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+
+    def time_fwd(descs, flags):
+        def fwd(i):
+            j = i % nrot
+            rc = lib.svdq_linear_forward(C.byref(descs[j]), S._t_ptr(Xs[j]), M, K, S._t_ptr(Ys[j]), N,
+                                         S._t_ptr(wss[j]), wsb, flags, sh)
+            if rc != 0:
+                raise S.SvdqError("svdq_linear_forward", rc)
+        for i in range(args.warmup):
+            fwd(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fwd(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    runs = {"w4a4": [], "fused": [], "unfused": []}
+    for _ in range(3):              # interleaved rounds, medians reported
+        runs["w4a4"].append(time_fwd(plain, 0))
+        runs["fused"].append(time_fwd(layers, 0))
+        runs["unfused"].append(time_fwd(layers, S.FLAG_UNFUSED_LOWRANK))
+    t0, tf, tu = (float(np.median(runs[k])) for k in ("w4a4", "fused", "unfused"))
+    print(json.dumps({
+        "study": "low-rank branch cost over the W4A4 forward: fused vs separate passes",
+        "workload": f"flux_{args.workload}_{M}x{K}x{N}", "format": fmt_name, "rank": args.rank,
+        "activation_dtype": dts, "rotating_buffer_sets": nrot, "steps": args.steps, "rounds": 3,
+        "t_w4a4_us": round(t0, 2), "t_fused_us": round(tf, 2), "t_unfused_us": round(tu, 2),
+        "overhead_fused_pct": round(100.0 * (tf - t0) / t0, 1),
+        "overhead_unfused_pct": round(100.0 * (tu - t0) / t0, 1),
+        "runs_us": {k: [round(x, 2) for x in v] for k, v in runs.items()}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -145,6 +226,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.lowrank_study:
+        lowrank_study(args)
         return
     import torch
     from diffusion_smooth_group_amd import svdq as S

@@ -173,7 +173,9 @@ constexpr int K1_IL_LDS_MAX_K = 16384;
 template <int NJT> struct K1Chunk { static constexpr int value = NJT <= 2 ? 6 : (NJT <= 4 ? 3 : 2); };
 template <int NJT> struct K1LRing { static constexpr int value = NJT <= 4 ? 2 : 1; };
 
-template <int FMT, int DT, int NJT, bool IL_LDS>
+// QUANT = false runs the down-projection alone (the unfused low-rank
+// baseline's separate pass over X): no codes, scales or invlambda.
+template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true>
 __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves per SIMD at least
   // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction buffer
   extern __shared__ __attribute__((aligned(16))) uint8_t k1_lds[];
@@ -344,7 +346,8 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       }
     }
 #pragma unroll
-    for (int d = 0; d < CH; ++d) quantize(xr[d], step_of(i0 + d));
+    for (int d = 0; d < CH; ++d)
+      if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
     // down-projection T^T += L1x^T X^T on the raw 16-bit inputs (padding
     // steps past the wave's last contribute zero)
 #pragma unroll
@@ -941,6 +944,104 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   }
 }
 
+// ------------------------------------------- unfused low-rank up-projection
+// The unfused low-rank baseline's last pass: Y = round16(GELU?(Y + T L2)),
+// reading and rewriting the 4-bit GEMM's rounded output.  Same fragment
+// layouts and 16-bit MFMAs as the GEMM's fused low-rank steps: MXFP4
+// layers use 32 x 32 x 16 tiles and 16-rank chunks, INT4 layers
+// 16 x 16 x 32 tiles and 32-rank chunks.
+struct UpParams {
+  const uint16_t* l2;
+  const uint16_t* t;
+  uint16_t* Y;
+  int64_t ldy, M, N;
+  int slots, nchunks;    // rank slots; MFMA K chunks of the active rank
+};
+
+// A wave owns ROWS tokens x 128 columns.  Its Y rows are loaded first, as
+// 16-byte pieces of whole rows (16 lanes per 256-byte row piece), so the
+// loads run under the MFMAs; the fp32 products then go through LDS into the
+// same row order, and each lane adds, rounds and stores its pieces.
+template <int DT, int FMT, bool GELU>
+__global__ __launch_bounds__(256) void k_up(UpParams p) {
+  constexpr bool MX = FMT == SVDQ_FMT_MXFP4_G32;
+  constexpr int ROWS = MX ? 32 : 16;             // tokens per wave
+  constexpr int PITCH = 128 * 4 + 16;            // bytes per staged fp32 row
+  constexpr int PIECES = ROWS * 16 / 64;         // 16-byte Y pieces per lane
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4 * ROWS * PITCH];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t n0 = int64_t(blockIdx.x) * 128;
+  const int64_t m0 = int64_t(blockIdx.y) * (4 * ROWS) + ROWS * wave;
+  if (m0 >= p.M) return;
+  uint8_t* st = stage + wave * ROWS * PITCH;
+  // Y pieces: piece c = 64 it + lane is row c / 16, columns 8 (c % 16) .. +8
+  u32x4 y[PIECES];
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int c = 64 * it + lane, row = c >> 4, col = (c & 15) * 8;
+    y[it] = m0 + row < p.M ? *reinterpret_cast<const u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col)
+                           : u32x4{0u, 0u, 0u, 0u};
+  }
+  if constexpr (MX) {
+    // 4 tiles of 32 x 32 x 16, 16-rank chunks
+    const int cs = p.slots / 16;
+    const u32x4* tb = reinterpret_cast<const u32x4*>(p.t) + (m0 / 32) * cs * 64 + lane;
+    const u32x4* lb = reinterpret_cast<const u32x4*>(p.l2) + (n0 / 32) * cs * 64 + lane;
+    f32x16 acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    for (int c = 0; c < p.nchunks; ++c) {
+      const u32x4 b = tb[c * 64];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mfma32x16<DT>(lb[(i * cs + c) * 64], b, acc[i]);
+    }
+    // accumulator 4gg + x of tile i: column 32i + 8gg + 4(lane / 32) + x, token lane % 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        *reinterpret_cast<f32x4*>(st + (lane & 31) * PITCH + (32 * i + 8 * gg + 4 * (lane >> 5)) * 4) =
+            f32x4{acc[i][4 * gg], acc[i][4 * gg + 1], acc[i][4 * gg + 2], acc[i][4 * gg + 3]};
+  } else {
+    // 8 tiles of 16 x 16 x 32, 32-rank chunks
+    const int cs = p.slots / 32;
+    const u32x4* tb = reinterpret_cast<const u32x4*>(p.t) + (m0 / 16) * cs * 64 + lane;
+    const u32x4* lb = reinterpret_cast<const u32x4*>(p.l2) + (n0 / 16) * cs * 64 + lane;
+    f32x4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < p.nchunks; ++c) {
+      const u32x4 b = tb[c * 64];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = mfma16<DT>(lb[(i * cs + c) * 64], b, acc[i]);
+    }
+    // accumulator x of tile i: column 16i + 4(lane / 16) + x, token lane % 16
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<f32x4*>(st + (lane & 15) * PITCH + (16 * i + 4 * (lane >> 4)) * 4) = acc[i];
+  }
+  SVDQ_WAIT_LGKM0();                 // the wave reads back only its own rows
+#pragma unroll
+  for (int it = 0; it < PIECES; ++it) {
+    const int c = 64 * it + lane, row = c >> 4, col = (c & 15) * 8;
+    if (m0 + row >= p.M) continue;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(st + row * PITCH + col * 4);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(st + row * PITCH + col * 4 + 16);
+    float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    unsigned o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float lo = h2f<DT>(y[it][e] & 0xFFFFu) + v[2 * e], hi = h2f<DT>(y[it][e] >> 16) + v[2 * e + 1];
+      if constexpr (GELU) {
+        lo = gelu_erf(lo);
+        hi = gelu_erf(hi);
+      }
+      o[e] = pack2<DT>(lo, hi);
+    }
+    *reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 // -------------------------------------------------- INT4 per-group products
 struct PartialParams {
   const uint8_t* wq;
@@ -1010,6 +1111,16 @@ void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
   }
 }
 
+// the down-projection alone (njt > 0)
+template <int FMT, int DT>
+void launch_k1_proj(const K1Params& kp, int64_t Mp, hipStream_t st) {
+  const dim3 grid(unsigned(Mp / 16)), block(256);
+  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
+  if (kp.njt <= 2) hipLaunchKernelGGL((k1_act<FMT, DT, 2, false, false>), grid, block, red_bytes(2), st, kp);
+  else if (kp.njt <= 4) hipLaunchKernelGGL((k1_act<FMT, DT, 4, false, false>), grid, block, red_bytes(4), st, kp);
+  else hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, false, false>), grid, block, red_bytes(MAXJT), st, kp);
+}
+
 template <int DT>
 void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
@@ -1030,11 +1141,126 @@ void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipSt
   else hipLaunchKernelGGL((k2_mx<DT, false>), dim3(T), dim3(256), 0, st, mp);
 }
 
+template <int DT, int FMT>
+void launch_k_up(const UpParams& up, bool gelu, hipStream_t st) {
+  const int rows = FMT == SVDQ_FMT_MXFP4_G32 ? 128 : 64;
+  const dim3 grid(unsigned(up.N / 128), unsigned(svdq::ceil_div(up.M, rows)));
+  if (gelu) hipLaunchKernelGGL((k_up<DT, FMT, true>), grid, dim3(256), 0, st, up);
+  else hipLaunchKernelGGL((k_up<DT, FMT, false>), grid, dim3(256), 0, st, up);
+}
+
 svdq_status check_device_layer(const svdq_layer* L) {
   svdq_status s = svdq::validate_layer(L);
   if (s != SVDQ_OK) return s;
   if (!L->blob_on_device) return SVDQ_ERR_INVALID_ARG;
   if (!aligned(L->blob, 256)) return SVDQ_ERR_INVALID_ARG;
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+namespace {
+
+enum K1Mode { K1_BOTH, K1_QUANT, K1_PROJ };
+
+// K1 on checked arguments: codes and scales, T, or both
+void run_k1(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx, uint8_t* ws, const svdq::WsOffsets& w,
+            K1Mode mode, hipStream_t stream) {
+  const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
+  K1Params kp;
+  kp.X = static_cast<const uint16_t*>(X_dev);
+  kp.ldx = ldx; kp.M = M; kp.K = L->K;
+  kp.invlam = reinterpret_cast<const float*>(blob + L->off_invlam);
+  kp.l1x = reinterpret_cast<const uint16_t*>(blob + L->off_l1x);
+  kp.slots = L->rank_slots;
+  kp.njt = mode == K1_QUANT ? 0
+           : L->fmt == SVDQ_FMT_MXFP4_G32 ? int(svdq::ceil_div(L->rank_active, 16))
+                                         : 2 * int(svdq::ceil_div(L->rank_active, 32));
+  kp.xq = ws + w.xq; kp.sx = ws + w.sx; kp.t = reinterpret_cast<uint16_t*>(ws + w.t);
+  if (mode == K1_PROJ) {
+    if (kp.njt == 0) return;
+    if (L->fmt == SVDQ_FMT_INT4_G64) {
+      if (L->dtype == SVDQ_BF16) launch_k1_proj<SVDQ_FMT_INT4_G64, SVDQ_BF16>(kp, w.Mp, stream);
+      else launch_k1_proj<SVDQ_FMT_INT4_G64, SVDQ_F16>(kp, w.Mp, stream);
+    } else {
+      if (L->dtype == SVDQ_BF16) launch_k1_proj<SVDQ_FMT_MXFP4_G32, SVDQ_BF16>(kp, w.Mp, stream);
+      else launch_k1_proj<SVDQ_FMT_MXFP4_G32, SVDQ_F16>(kp, w.Mp, stream);
+    }
+    return;
+  }
+  if (L->fmt == SVDQ_FMT_INT4_G64) {
+    if (L->dtype == SVDQ_BF16) launch_k1<SVDQ_FMT_INT4_G64, SVDQ_BF16>(kp, w.Mp, stream);
+    else launch_k1<SVDQ_FMT_INT4_G64, SVDQ_F16>(kp, w.Mp, stream);
+  } else {
+    if (L->dtype == SVDQ_BF16) launch_k1<SVDQ_FMT_MXFP4_G32, SVDQ_BF16>(kp, w.Mp, stream);
+    else launch_k1<SVDQ_FMT_MXFP4_G32, SVDQ_F16>(kp, w.Mp, stream);
+  }
+}
+
+// K2 on checked arguments; lowrank = false leaves the low-rank branch out
+void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
+            bool gelu, bool lowrank, hipStream_t stream) {
+  const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
+  K2Params kp;
+  kp.wq = blob + L->off_wq;
+  kp.sw = blob + L->off_sw;
+  kp.l2 = reinterpret_cast<const uint16_t*>(blob + L->off_l2);
+  kp.bias = reinterpret_cast<const float*>(blob + L->off_bias);
+  kp.xq = ws + w.xq; kp.sx = ws + w.sx;
+  kp.t = reinterpret_cast<const uint16_t*>(ws + w.t);
+  kp.Y = static_cast<uint16_t*>(Y_dev);
+  kp.ldy = ldy; kp.M = M; kp.N = L->N; kp.K = L->K;
+  kp.slots = L->rank_slots;
+  const int ra = lowrank ? L->rank_active : 0;
+  kp.nchunks = int(svdq::ceil_div(ra, 32));
+  kp.nchunks16 = int(svdq::ceil_div(ra, 16));
+  if (L->fmt == SVDQ_FMT_INT4_G64) {
+    if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
+    else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
+  } else {
+    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w, gelu, stream);
+    else launch_k2_mx<SVDQ_F16>(kp, w, gelu, stream);
+  }
+}
+
+// the unfused baseline's up-projection pass: Y = round16(GELU?(Y + T L2))
+void run_up(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
+            bool gelu, hipStream_t stream) {
+  const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
+  UpParams up;
+  up.l2 = reinterpret_cast<const uint16_t*>(blob + L->off_l2);
+  up.t = reinterpret_cast<const uint16_t*>(ws + w.t);
+  up.Y = static_cast<uint16_t*>(Y_dev);
+  up.ldy = ldy; up.M = M; up.N = L->N;
+  up.slots = L->rank_slots;
+  const bool mx = L->fmt == SVDQ_FMT_MXFP4_G32;
+  up.nchunks = int(svdq::ceil_div(L->rank_active, mx ? 16 : 32));
+  if (mx) {
+    if (L->dtype == SVDQ_BF16) launch_k_up<SVDQ_BF16, SVDQ_FMT_MXFP4_G32>(up, gelu, stream);
+    else launch_k_up<SVDQ_F16, SVDQ_FMT_MXFP4_G32>(up, gelu, stream);
+  } else {
+    if (L->dtype == SVDQ_BF16) launch_k_up<SVDQ_BF16, SVDQ_FMT_INT4_G64>(up, gelu, stream);
+    else launch_k_up<SVDQ_F16, SVDQ_FMT_INT4_G64>(up, gelu, stream);
+  }
+}
+
+constexpr unsigned SVDQ_FLAGS_ALL = unsigned(SVDQ_FLAG_GELU) | unsigned(SVDQ_FLAG_UNFUSED_LOWRANK);
+
+svdq_status check_x(const svdq_layer* L, const void* X_dev, int64_t ldx) {
+  if (!X_dev) return SVDQ_ERR_INVALID_ARG;
+  if (ldx < L->K || ldx % 8 != 0 || !aligned(X_dev, 16)) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+svdq_status check_y(const svdq_layer* L, const void* Y_dev, int64_t ldy) {
+  if (!Y_dev) return SVDQ_ERR_INVALID_ARG;
+  if (ldy < L->N || ldy % 8 != 0 || !aligned(Y_dev, 16)) return SVDQ_ERR_SHAPE;
+  return SVDQ_OK;
+}
+svdq_status check_ws(const svdq_layer* L, int64_t M, const void* ws_dev, size_t ws_bytes, svdq::WsOffsets* w) {
+  if (!ws_dev) return SVDQ_ERR_INVALID_ARG;
+  *w = svdq::ws_offsets(M, L->K, L->rank_slots, L->fmt);
+  if (ws_bytes < w->total) return SVDQ_ERR_CAPACITY;
+  if (!aligned(ws_dev, 256)) return SVDQ_ERR_INVALID_ARG;
   return SVDQ_OK;
 }
 
@@ -1046,29 +1272,9 @@ extern "C" svdq_status svdq_quantize_activations(const svdq_layer* L, const void
   if (st != SVDQ_OK) return st;
   if (M < 0) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
-  if (!X_dev || !ws_dev) return SVDQ_ERR_INVALID_ARG;
-  if (ldx < L->K || ldx % 8 != 0 || !aligned(X_dev, 16)) return SVDQ_ERR_SHAPE;
-  svdq::WsOffsets w = svdq::ws_offsets(M, L->K, L->rank_slots, L->fmt);
-  if (ws_bytes < w.total) return SVDQ_ERR_CAPACITY;
-  if (!aligned(ws_dev, 256)) return SVDQ_ERR_INVALID_ARG;
-  const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
-  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  K1Params kp;
-  kp.X = static_cast<const uint16_t*>(X_dev);
-  kp.ldx = ldx; kp.M = M; kp.K = L->K;
-  kp.invlam = reinterpret_cast<const float*>(blob + L->off_invlam);
-  kp.l1x = reinterpret_cast<const uint16_t*>(blob + L->off_l1x);
-  kp.slots = L->rank_slots;
-  kp.njt = L->fmt == SVDQ_FMT_MXFP4_G32 ? int(svdq::ceil_div(L->rank_active, 16))
-                                        : 2 * int(svdq::ceil_div(L->rank_active, 32));
-  kp.xq = ws + w.xq; kp.sx = ws + w.sx; kp.t = reinterpret_cast<uint16_t*>(ws + w.t);
-  if (L->fmt == SVDQ_FMT_INT4_G64) {
-    if (L->dtype == SVDQ_BF16) launch_k1<SVDQ_FMT_INT4_G64, SVDQ_BF16>(kp, w.Mp, stream);
-    else launch_k1<SVDQ_FMT_INT4_G64, SVDQ_F16>(kp, w.Mp, stream);
-  } else {
-    if (L->dtype == SVDQ_BF16) launch_k1<SVDQ_FMT_MXFP4_G32, SVDQ_BF16>(kp, w.Mp, stream);
-    else launch_k1<SVDQ_FMT_MXFP4_G32, SVDQ_F16>(kp, w.Mp, stream);
-  }
+  svdq::WsOffsets w;
+  if ((st = check_x(L, X_dev, ldx)) != SVDQ_OK || (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK) return st;
+  run_k1(L, X_dev, M, ldx, static_cast<uint8_t*>(ws_dev), w, K1_BOTH, stream);
   return launch_ok();
 }
 
@@ -1078,33 +1284,9 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
   if (st != SVDQ_OK) return st;
   if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
-  if (!Y_dev || !ws_dev) return SVDQ_ERR_INVALID_ARG;
-  if (ldy < L->N || ldy % 8 != 0 || !aligned(Y_dev, 16)) return SVDQ_ERR_SHAPE;
-  svdq::WsOffsets w = svdq::ws_offsets(M, L->K, L->rank_slots, L->fmt);
-  if (ws_bytes < w.total) return SVDQ_ERR_CAPACITY;
-  if (!aligned(ws_dev, 256)) return SVDQ_ERR_INVALID_ARG;
-  const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
-  const uint8_t* ws = static_cast<const uint8_t*>(ws_dev);
-  K2Params kp;
-  kp.wq = blob + L->off_wq;
-  kp.sw = blob + L->off_sw;
-  kp.l2 = reinterpret_cast<const uint16_t*>(blob + L->off_l2);
-  kp.bias = reinterpret_cast<const float*>(blob + L->off_bias);
-  kp.xq = ws + w.xq; kp.sx = ws + w.sx;
-  kp.t = reinterpret_cast<const uint16_t*>(ws + w.t);
-  kp.Y = static_cast<uint16_t*>(Y_dev);
-  kp.ldy = ldy; kp.M = M; kp.N = L->N; kp.K = L->K;
-  kp.slots = L->rank_slots;
-  kp.nchunks = int(svdq::ceil_div(L->rank_active, 32));
-  kp.nchunks16 = int(svdq::ceil_div(L->rank_active, 16));
-  const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
-  if (L->fmt == SVDQ_FMT_INT4_G64) {
-    if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
-  } else {
-    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w, gelu, stream);
-    else launch_k2_mx<SVDQ_F16>(kp, w, gelu, stream);
-  }
+  svdq::WsOffsets w;
+  if ((st = check_y(L, Y_dev, ldy)) != SVDQ_OK || (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK) return st;
+  run_k2(L, M, Y_dev, ldy, static_cast<const uint8_t*>(ws_dev), w, (flags & SVDQ_FLAG_GELU) != 0u, true, stream);
   return launch_ok();
 }
 
@@ -1113,13 +1295,26 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
                                            hipStream_t stream) {
   svdq_status st = check_device_layer(L);
   if (st != SVDQ_OK) return st;
-  if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || (flags & ~SVDQ_FLAGS_ALL) != 0u) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
-  if (!Y_dev) return SVDQ_ERR_INVALID_ARG;
-  if (ldy < L->N || ldy % 8 != 0 || !aligned(Y_dev, 16)) return SVDQ_ERR_SHAPE;
-  st = svdq_quantize_activations(L, X_dev, M, ldx, ws_dev, ws_bytes, stream);
-  if (st != SVDQ_OK) return st;
-  return svdq_gemm_forward(L, M, Y_dev, ldy, ws_dev, ws_bytes, flags, stream);
+  svdq::WsOffsets w;
+  if ((st = check_x(L, X_dev, ldx)) != SVDQ_OK || (st = check_y(L, Y_dev, ldy)) != SVDQ_OK ||
+      (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK)
+    return st;
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
+  if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) == 0u || L->rank_active == 0) {
+    run_k1(L, X_dev, M, ldx, ws, w, K1_BOTH, stream);
+    run_k2(L, M, Y_dev, ldy, ws, w, gelu, true, stream);
+  } else {
+    // the low-rank branch as separate passes: quantize, down-project (a
+    // second read of X), 4-bit GEMM + bias, then Y += T L2 (+ GELU)
+    run_k1(L, X_dev, M, ldx, ws, w, K1_QUANT, stream);
+    run_k1(L, X_dev, M, ldx, ws, w, K1_PROJ, stream);
+    run_k2(L, M, Y_dev, ldy, ws, w, false, false, stream);
+    run_up(L, M, Y_dev, ldy, ws, w, gelu, stream);
+  }
+  return launch_ok();
 }
 
 extern "C" svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int64_t ldx,

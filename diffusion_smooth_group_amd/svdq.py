@@ -22,6 +22,7 @@ FMT_MXFP4_G32 = 1
 F16 = 0
 BF16 = 1
 FLAG_GELU = 1
+FLAG_UNFUSED_LOWRANK = 2
 MAX_RANK_CAPACITY = 128
 
 FMT_CODES = {"int4_g64": FMT_INT4_G64, "mxfp4_g32": FMT_MXFP4_G32}
@@ -259,15 +260,18 @@ class SVDQLinear:
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.blob.device)
         return self._ws
 
-    def forward(self, X, gelu: bool = False, Y=None, ws=None, stream=None):
+    def forward(self, X, gelu: bool = False, Y=None, ws=None, stream=None, unfused: bool = False):
+        """unfused=True runs the low-rank branch as separate passes (the
+        baseline the fused kernels are measured against)."""
         import torch
         assert X.dim() == 2 and X.shape[1] == self.K and X.stride(1) == 1
         M = X.shape[0]
         if Y is None:
             Y = torch.empty((M, self.N), dtype=X.dtype, device=X.device)
         ws = self.workspace(M) if ws is None else ws
+        flags = (FLAG_GELU if gelu else 0) | (FLAG_UNFUSED_LOWRANK if unfused else 0)
         _call("svdq_linear_forward", C.byref(self.layer), _t_ptr(X), M, X.stride(0), _t_ptr(Y), Y.stride(0),
-              _t_ptr(ws), ws.numel(), FLAG_GELU if gelu else 0, _stream(stream))
+              _t_ptr(ws), ws.numel(), flags, _stream(stream))
         return Y
 
     __call__ = forward

@@ -56,7 +56,12 @@ typedef enum {
 typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 
 enum {
-  SVDQ_FLAG_GELU = 1u        /* apply x * Phi(x) (erf GELU) to Y before rounding */
+  SVDQ_FLAG_GELU = 1u,            /* apply x * Phi(x) (erf GELU) to Y before rounding */
+  SVDQ_FLAG_UNFUSED_LOWRANK = 2u  /* baseline for measuring the fusion: run the low-rank
+                                     branch as separate passes (a second read of X for T,
+                                     then Y is read back and rewritten with T L2 added),
+                                     as an engine without the fusion would; Y is rounded
+                                     twice.  svdq_linear_forward only. */
 };
 
 #define SVDQ_MAX_RANK_CAPACITY 128
@@ -137,7 +142,8 @@ svdq_status svdq_detach_lora(svdq_layer* layer, hipStream_t stream);
 svdq_status svdq_workspace_size(const svdq_layer* layer, int64_t M, size_t* bytes);
 
 /* Y = X_hat L1x L2 + Q(X_hat) Q(R) + bias [-> GELU], rounded to the layer's
- * dtype (SVDQuant §4.2 Eq. 5, fused as in §4.3).  Two kernels on `stream`:
+ * dtype (SVDQuant §4.2 Eq. 5, fused as in §4.3).  flags: SVDQ_FLAG_GELU,
+ * SVDQ_FLAG_UNFUSED_LOWRANK (see above).  Two kernels on `stream`:
  * the activation kernel (smoothing, group quantization, down-projection,
  * one pass over X) and the 4-bit GEMM with the up-projection, bias and
  * optional GELU in its epilogue.  X_dev: M x K (ldx >= K, ldx % 8 == 0,

@@ -63,7 +63,7 @@ def compare_outputs(Y_gpu_bits, Y_ref_bits, dtype, what=""):
 
 
 def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, cap=None, alpha=1.0,
-                   check_codes=True):
+                   check_codes=True, unfused=False):
     """Pack on the GPU, run the forward, and compare with the oracle.
     rows / cols: sample of outputs evaluated by the oracle (None = all)."""
     import torch
@@ -78,7 +78,7 @@ def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, c
                    absmax=absmax)
     if lora:
         lin.attach_lora(d["lora_A"], d["lora_B"], alpha)
-    Y = lin.forward(Xd, gelu=gelu)
+    Y = lin.forward(Xd, gelu=gelu, unfused=unfused)
     torch.cuda.synchronize()
     Yb = S.device_to_bits(Y)
     ex = lin.export()

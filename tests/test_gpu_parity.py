@@ -51,6 +51,26 @@ def test_short_k_wide_low_rank(fmt, K):
     G.run_layer_case(d, fmt, 16, lora=True)
 
 
+@pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
+@pytest.mark.parametrize("dtype", [o.BF16, o.F16])
+def test_unfused_lowrank_baseline(fmt, dtype):
+    # the separate-pass low-rank branch (Y rounded after the 4-bit GEMM and
+    # again after T L2 is added) meets the same gates against the oracle,
+    # with LoRA columns, GELU after the sum and a ragged token count
+    d = _small(150, 512, 384, dtype, fmt, 32, lora=16, seed=60)
+    G.run_layer_case(d, fmt, 32, lora=True, gelu=True, unfused=True)
+
+
+def test_unfused_lowrank_qkv_sampled():
+    spec = wl.config_shapes(2)[0]
+    d = wl.generate(spec)
+    rows, cols = _sample(spec.M, spec.N, 61)
+    G.run_layer_case(d, o.INT4, 32, rows=rows, cols=cols, unfused=True)
+    d5 = wl.generate(wl.config_shapes(5)[0])
+    rows, cols = _sample(d5["spec"].M, d5["spec"].N, 62)
+    G.run_layer_case(d5, o.MXFP4, 32, lora=True, rows=rows, cols=cols, unfused=True)
+
+
 @pytest.mark.parametrize("M", [1, 17, 256, 300])
 def test_token_counts(M):
     d = _small(M, 256, 128, o.F16, o.INT4, 8, seed=3 + M)
