@@ -621,6 +621,10 @@ struct MxParams {
   int64_t ldy, M, N, K;
   int slots, nchunks16;
   int tiles_n, tiles_m;
+  // byte offsets of the weight-side regions from l2 (all in the layer blob)
+  // and of the token-side regions from xq (all in the workspace); both spans
+  // are below 2 GiB, so the stage loads take them as scalar offsets
+  int off_wq, off_sw, off_sx, off_t;
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -701,26 +705,36 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     }
     int64_t pn = n0 / 64 + wave;
     pn = pn < p.N / 64 ? pn : p.N / 64 - 1;
-    const uint8_t* gsa = p.sw + (pn * nsteps) * 256 + lane * 4;
-    const uint8_t* gsb = p.sx + ((m0 / 64 + wave) * nsteps) * 256 + lane * 4;
-    const uint8_t* l2b = reinterpret_cast<const uint8_t*>(p.l2) + lane * 16;
-    const uint8_t* ttb = reinterpret_cast<const uint8_t*>(p.t) + lane * 16;
-    // this wave's fixed source addresses; step r adds r * 2048 (fragments)
+    const int osa = p.off_sw + int(pn * nsteps) * 256;
+    const int osb = p.off_sx + int((m0 / 64 + wave) * nsteps) * 256;
+    // Stage loads are buffer loads straight into LDS: one descriptor over the
+    // blob (L2, codes, scales), one over the workspace (codes, scales, T);
+    // each load takes a scalar byte offset plus the lane's offset, so no
+    // 64-bit per-lane address is computed or kept in vector registers.
+    const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)p.l2, 0, -1, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, 0, -1, 0x00020000);
+    const int lo16 = lane * 16, lo4 = lane * 4;
+    auto dma16 = [&](__amdgpu_buffer_rsrc_t rs, int soff, uint8_t* dst) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 16, lo16, soff, 0, 0);
+    };
+    auto dma4 = [&](__amdgpu_buffer_rsrc_t rs, int soff, uint8_t* dst) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, lo4, soff, 0, 0);
+    };
+    // this wave's fixed source offsets; step r adds r * 2048 (fragments)
     // or r * 256 (scales)
-    const uint8_t* ga[4];
-    const uint8_t* gb[4];
+    int ga[4], gb[4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int h = (4 * wave + f) & 1;
-      ga[f] = p.wq + (tA[f] * nsteps * 2 + h) * 1024 + lane * 16;
-      gb[f] = p.xq + (tB[f] * nsteps * 2 + h) * 1024 + lane * 16;
+      ga[f] = p.off_wq + int(tA[f] * nsteps * 2 + h) * 1024;
+      gb[f] = int(tB[f] * nsteps * 2 + h) * 1024;
     }
     // one of the 10 loads a wave issues per K step
     auto issue_unit = [&](int r, uint8_t* base, int x) {
-      if (x < 4) lds_load16(ga[x] + int64_t(r) * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
-      else if (x < 8) lds_load16(gb[x - 4] + int64_t(r) * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
-      else if (x == 8) lds_load4(gsa + int64_t(r) * 256, base + mx::SA_OFF + wave * 256);
-      else lds_load4(gsb + int64_t(r) * 256, base + mx::SB_OFF + wave * 256);
+      if (x < 4) dma16(rsb, ga[x] + r * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
+      else if (x < 8) dma16(rsw, gb[x - 4] + r * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
+      else if (x == 8) dma4(rsb, osa + r * 256, base + mx::SA_OFF + wave * 256);
+      else dma4(rsw, osb + r * 256, base + mx::SB_OFF + wave * 256);
     };
     // the 10 loads of low-rank step e: chunks 2e, 2e+1 of L2 and T (the scale
     // slots reload the first step's scales so every step issues 10 loads)
@@ -730,11 +744,11 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         const int h = (4 * wave + f) & 1;
         int c = 2 * e + h;
         c = c < p.nchunks16 ? c : p.nchunks16 - 1;
-        lds_load16(l2b + (tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
-        lds_load16(ttb + (tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
+        dma16(rsb, int(tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
+        dma16(rsw, p.off_t + int(tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
       }
-      lds_load4(gsa, base + mx::SA_OFF + wave * 256);
-      lds_load4(gsb, base + mx::SB_OFF + wave * 256);
+      dma4(rsb, osa, base + mx::SA_OFF + wave * 256);
+      dma4(rsw, osb, base + mx::SB_OFF + wave * 256);
     };
     auto issue = [&](int r, int st) {
       uint8_t* base = smem + st * mx::STAGE_BYTES;
@@ -1136,6 +1150,10 @@ void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipSt
   mp.nchunks16 = kp.nchunks16;
   mp.tiles_n = int(svdq::ceil_div(kp.N, 256));
   mp.tiles_m = int(w.Mp / 256);
+  mp.off_wq = int(kp.wq - reinterpret_cast<const uint8_t*>(kp.l2));
+  mp.off_sw = int(kp.sw - reinterpret_cast<const uint8_t*>(kp.l2));
+  mp.off_sx = int(kp.sx - kp.xq);
+  mp.off_t = int(reinterpret_cast<const uint8_t*>(kp.t) - kp.xq);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
   if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), dim3(T), dim3(256), 0, st, mp);
   else hipLaunchKernelGGL((k2_mx<DT, false>), dim3(T), dim3(256), 0, st, mp);
@@ -1223,6 +1241,14 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
   }
 }
 
+// the MXFP4 GEMM addresses the blob from L2 and the workspace from the
+// activation codes with 31-bit offsets
+bool mx_offsets_fit(const svdq_layer* L, const svdq::WsOffsets& w) {
+  if (L->fmt != SVDQ_FMT_MXFP4_G32) return true;
+  const size_t lim = size_t(1) << 31;
+  return L->off_bias + size_t(L->N) * 4 - L->off_l2 < lim && w.total - w.xq < lim;
+}
+
 // the unfused baseline's up-projection pass: Y = round16(GELU?(Y + T L2))
 void run_up(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
             bool gelu, hipStream_t stream) {
@@ -1286,6 +1312,7 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
   if (M == 0) return SVDQ_OK;
   svdq::WsOffsets w;
   if ((st = check_y(L, Y_dev, ldy)) != SVDQ_OK || (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK) return st;
+  if (!mx_offsets_fit(L, w)) return SVDQ_ERR_UNSUPPORTED;
   run_k2(L, M, Y_dev, ldy, static_cast<const uint8_t*>(ws_dev), w, (flags & SVDQ_FLAG_GELU) != 0u, true, stream);
   return launch_ok();
 }
@@ -1301,6 +1328,7 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
   if ((st = check_x(L, X_dev, ldx)) != SVDQ_OK || (st = check_y(L, Y_dev, ldy)) != SVDQ_OK ||
       (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK)
     return st;
+  if (!mx_offsets_fit(L, w)) return SVDQ_ERR_UNSUPPORTED;
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
   if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) == 0u || L->rank_active == 0) {
