@@ -96,12 +96,14 @@ namespace {
 // Core pack into a host byte buffer.
 svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int dtype, const float* absmax,
                       int rank, int capacity, int fmt, const void* bias_host, uint8_t* blob, size_t bytes,
-                      svdq_layer* out, int on_dev, void* blob_ptr_for_desc) {
+                      svdq_layer* out, int on_dev, void* blob_ptr_for_desc, int refine_iters = 0,
+                      double* errors = nullptr) {
   svdq_status st = check_common(K, N, capacity, fmt, dtype);
   if (st != SVDQ_OK) return st;
   if (!W_host || !out) return SVDQ_ERR_INVALID_ARG;
   if (ldw < N) return SVDQ_ERR_SHAPE;
   if (rank < 0 || rank > capacity || rank > std::min(K, N)) return SVDQ_ERR_INVALID_ARG;
+  if (refine_iters < 0 || refine_iters > SVDQ_MAX_REFINE_ITERS) return SVDQ_ERR_INVALID_ARG;
   const int slots = slots_for(capacity);
   BlobOffsets o = blob_offsets(K, N, slots, fmt);
   if (!blob || bytes < o.total) return SVDQ_ERR_CAPACITY;
@@ -139,78 +141,155 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
     lam[j] = l;
     invlam[j] = 1.0f / l;
   }
-  // W_hat = diag(lambda) W (exact in float64) and its rank-r split
-  std::vector<uint16_t> l1x(size_t(K) * std::max(rank, 1), 0), l2q(size_t(std::max(rank, 1)) * N, 0);
-  if (rank > 0) {
-    std::vector<double> A(size_t(K) * N);
-    parallel_for(K, [&](int64_t b, int64_t e) {
-      for (int64_t j = b; j < e; ++j)
-        for (int64_t n = 0; n < N; ++n) A[size_t(j) * N + n] = double(lam[j]) * double(W[size_t(j) * N + n]);
-    });
+  // One candidate split: 16-bit factors, the fp32 residual's codes and
+  // scales per output column (canonical [N][K] / [N][K/G]), and its error.
+  const int G = group_size(fmt);
+  const int rk = std::max(rank, 1);
+  struct Cand {
+    std::vector<uint16_t> l1x, l2q;   // K x rank, rank x N
+    std::vector<uint8_t> q;           // INT4: int8 value; MXFP4: E2M1 code
+    std::vector<uint16_t> sc;         // INT4: fp16 bits; MXFP4: e8m0
+    double err = 0.0;
+  };
+  auto what = [&](int64_t j, int64_t n) { return double(lam[j]) * double(W[size_t(j) * N + n]); };
+  // low-rank term at row j: s[n] = sum_k L1x[j,k] L2q[k,n], k ascending (float64)
+  auto lowrank_row = [&](const Cand& c, int64_t j, std::vector<double>& srow, const std::vector<double>& l2d) {
+    std::fill(srow.begin(), srow.end(), 0.0);
+    for (int k = 0; k < rank; ++k) {
+      double a = h16_to_f32(c.l1x[size_t(j) * rank + k], dtype);
+      const double* l2r = &l2d[size_t(k) * N];
+      for (int64_t n = 0; n < N; ++n) srow[n] = srow[n] + a * l2r[n];
+    }
+  };
+  auto l2_double = [&](const Cand& c) {
+    std::vector<double> l2d(size_t(rk) * N, 0.0);
+    for (size_t i = 0; i < size_t(rank) * N; ++i) l2d[i] = h16_to_f32(c.l2q[i], dtype);
+    return l2d;
+  };
+  auto deq = [&](const Cand& c, int64_t n, int64_t k) -> double {
+    const size_t gi = size_t(n) * (K / G) + size_t(k / G);
+    if (fmt == SVDQ_FMT_INT4_G64)
+      return double(int8_t(c.q[size_t(n) * K + k])) * double(f16_to_f32(c.sc[gi]));
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    const uint8_t code = c.q[size_t(n) * K + k];
+    const double v = grid[code & 7] * std::ldexp(1.0, int(c.sc[gi]) - 127);
+    return (code & 8) ? -v : v;
+  };
+  // factors of the split of matrix B (K x N, float64), rounded to 16 bits
+  auto factors = [&](const std::vector<double>& B, Cand& c) -> bool {
+    c.l1x.assign(size_t(K) * rk, 0);
+    c.l2q.assign(size_t(rk) * N, 0);
+    if (rank == 0) return true;
     std::vector<double> L1(size_t(K) * rank), L2(size_t(rank) * N);
-    if (!truncated_svd(A.data(), K, N, rank, L1.data(), L2.data(), nullptr)) return SVDQ_ERR_NUMERIC;
+    if (!truncated_svd(B.data(), K, N, rank, L1.data(), L2.data(), nullptr)) return false;
     for (int64_t j = 0; j < K; ++j)
       for (int i = 0; i < rank; ++i)
-        l1x[size_t(j) * rank + i] = f64_to_h16_rne(double(invlam[j]) * L1[size_t(j) * rank + i], dtype);
-    for (size_t i = 0; i < size_t(rank) * N; ++i) l2q[i] = f64_to_h16_rne(L2[i], dtype);
-  }
-  // R = fl32(lambda W - lambda * sum_k L1x[:,k] L2q[k,:]), k ascending; stored transposed (N x K)
-  std::vector<float> Rt(size_t(N) * K);
-  {
-    std::vector<double> l1d(size_t(K) * std::max(rank, 1)), l2d(size_t(std::max(rank, 1)) * N);
-    for (size_t i = 0; i < size_t(K) * rank; ++i) l1d[i] = h16_to_f32(l1x[i], dtype);
-    for (size_t i = 0; i < size_t(rank) * N; ++i) l2d[i] = h16_to_f32(l2q[i], dtype);
+        c.l1x[size_t(j) * rank + i] = f64_to_h16_rne(double(invlam[j]) * L1[size_t(j) * rank + i], dtype);
+    for (size_t i = 0; i < size_t(rank) * N; ++i) c.l2q[i] = f64_to_h16_rne(L2[i], dtype);
+    return true;
+  };
+  // R = fl32(lambda W - lambda * sum_k L1x[:,k] L2q[k,:]), its group codes
+  // (per output column, groups along K), and the split's error
+  // ||W_hat - diag(lambda) L1x L2q - deq(Q(R))||_F^2 in float64
+  auto residual_codes = [&](Cand& c) {
+    std::vector<float> Rt(size_t(N) * K);
+    const std::vector<double> l2d = l2_double(c);
     parallel_for(K, [&](int64_t b, int64_t e) {
-      std::vector<double> s(N);
+      std::vector<double> srow(N);
       for (int64_t j = b; j < e; ++j) {
-        std::fill(s.begin(), s.end(), 0.0);
-        for (int k = 0; k < rank; ++k) {
-          double a = l1d[size_t(j) * rank + k];
-          const double* l2r = &l2d[size_t(k) * N];
-          for (int64_t n = 0; n < N; ++n) s[n] = s[n] + a * l2r[n];
-        }
-        double lj = double(lam[j]);
-        for (int64_t n = 0; n < N; ++n) {
-          double what = lj * double(W[size_t(j) * N + n]);
-          double d = lj * s[n];
-          Rt[size_t(n) * K + j] = float(what - d);
-        }
+        lowrank_row(c, j, srow, l2d);
+        const double lj = double(lam[j]);
+        for (int64_t n = 0; n < N; ++n) Rt[size_t(n) * K + j] = float(what(j, n) - lj * srow[n]);
       }
     });
+    c.q.assign(size_t(N) * K, 0);
+    c.sc.assign(size_t(N) * (K / G), 0);
+    parallel_for(N, [&](int64_t nb, int64_t ne) {
+      std::vector<int8_t> qi(64);
+      std::vector<uint8_t> qm(32);
+      for (int64_t n = nb; n < ne; ++n)
+        for (int64_t g = 0; g < K / G; ++g) {
+          const float* v = &Rt[size_t(n) * K + g * G];
+          uint8_t* qo = &c.q[size_t(n) * K + g * G];
+          if (fmt == SVDQ_FMT_INT4_G64) {
+            uint16_t sbits;
+            quant_int4_group(v, qi.data(), &sbits);
+            c.sc[size_t(n) * (K / G) + g] = sbits;
+            for (int i = 0; i < G; ++i) qo[i] = uint8_t(qi[i]);
+          } else {
+            uint8_t e;
+            quant_mx_group(v, qm.data(), &e);
+            c.sc[size_t(n) * (K / G) + g] = e;
+            for (int i = 0; i < G; ++i) qo[i] = qm[i];
+          }
+        }
+    });
+    std::vector<double> part(size_t(K), 0.0);
+    parallel_for(K, [&](int64_t b, int64_t e) {
+      std::vector<double> srow(N);
+      for (int64_t j = b; j < e; ++j) {
+        lowrank_row(c, j, srow, l2d);
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double d = what(j, n) - double(lam[j]) * srow[n] - deq(c, n, j);
+          acc += d * d;
+        }
+        part[j] = acc;
+      }
+    });
+    c.err = 0.0;
+    for (int64_t j = 0; j < K; ++j) c.err += part[j];
+  };
+
+  // one-shot split of W_hat = diag(lambda) W (exact in float64) [SVDQuant
+  // §4.2], then refine_iters rounds that split W_hat - deq(Q(R)) again and
+  // re-derive R; the split with the smallest error is kept
+  Cand best;
+  {
+    std::vector<double> A;
+    if (rank > 0) {
+      A.resize(size_t(K) * N);
+      parallel_for(K, [&](int64_t b, int64_t e) {
+        for (int64_t j = b; j < e; ++j)
+          for (int64_t n = 0; n < N; ++n) A[size_t(j) * N + n] = what(j, n);
+      });
+    }
+    if (!factors(A, best)) return SVDQ_ERR_NUMERIC;
+    residual_codes(best);
+    if (errors) errors[0] = best.err;
+    Cand cur = best;
+    for (int it = 1; it <= refine_iters && rank > 0; ++it) {
+      parallel_for(K, [&](int64_t b, int64_t e) {
+        for (int64_t j = b; j < e; ++j)
+          for (int64_t n = 0; n < N; ++n) A[size_t(j) * N + n] = what(j, n) - deq(cur, n, j);
+      });
+      Cand next;
+      if (!factors(A, next)) return SVDQ_ERR_NUMERIC;
+      residual_codes(next);
+      if (errors) errors[it] = next.err;
+      cur = std::move(next);
+      if (cur.err < best.err) best = cur;
+    }
   }
   std::memset(blob, 0, o.total);
-  // residual codes and scales, per output column, groups along K
-  const int G = group_size(fmt);
+  // residual codes and scales, tiled
   uint8_t* wq = blob + o.wq;
   uint8_t* sw = blob + o.sw;
   parallel_for(N / 16, [&](int64_t tb, int64_t te) {
-    std::vector<int8_t> qi(64);
-    std::vector<uint8_t> qm(32);
-    for (int64_t n = tb * 16; n < te * 16; ++n) {
-      const float* col = &Rt[size_t(n) * K];
+    for (int64_t n = tb * 16; n < te * 16; ++n)
       for (int64_t g = 0; g < K / G; ++g) {
-        if (fmt == SVDQ_FMT_INT4_G64) {
-          uint16_t s;
-          quant_int4_group(col + g * G, qi.data(), &s);
-          std::memcpy(sw + 2 * int4_wscale_pos(n, g, K), &s, 2);
-          for (int i = 0; i < G; ++i) {
-            size_t byte; int nib;
-            code_pos(n, g * G + i, K, fmt, &byte, &nib);
-            wq[byte] |= uint8_t((uint8_t(qi[i]) & 0xF) << (4 * nib));
-          }
-        } else {
-          uint8_t e;
-          quant_mx_group(col + g * G, qm.data(), &e);
-          sw[mx_scale_pos(n, g, K)] = e;
-          for (int i = 0; i < G; ++i) {
-            size_t byte; int nib;
-            code_pos(n, g * G + i, K, fmt, &byte, &nib);
-            wq[byte] |= uint8_t(qm[i] << (4 * nib));
-          }
+        const uint16_t sv = best.sc[size_t(n) * (K / G) + g];
+        if (fmt == SVDQ_FMT_INT4_G64) std::memcpy(sw + 2 * int4_wscale_pos(n, g, K), &sv, 2);
+        else sw[mx_scale_pos(n, g, K)] = uint8_t(sv);
+        for (int i = 0; i < G; ++i) {
+          size_t byte; int nib;
+          code_pos(n, g * G + i, K, fmt, &byte, &nib);
+          wq[byte] |= uint8_t((best.q[size_t(n) * K + g * G + i] & 0xF) << (4 * nib));
         }
       }
-    }
   });
+  const std::vector<uint16_t>& l1x = best.l1x;
+  const std::vector<uint16_t>& l2q = best.l2q;
   // factors, tiled
   uint16_t* l1t = reinterpret_cast<uint16_t*>(blob + o.l1x);
   uint16_t* l2t = reinterpret_cast<uint16_t*>(blob + o.l2);
@@ -284,6 +363,27 @@ extern "C" svdq_status svdq_pack_weights(const void* W_host, int64_t K, int64_t 
   if (st != SVDQ_OK) return st;
   out->blob_bytes = blob_bytes;
   return copy_bytes(blob_dev, 1, host.data(), 0, need, stream);
+}
+
+extern "C" svdq_status svdq_pack_weights_ex(const void* W_host, int64_t K, int64_t N, int64_t ldw, svdq_dtype dtype,
+                                            const float* act_absmax_host, int rank, int rank_capacity,
+                                            svdq_format fmt, const void* bias_host, int refine_iters,
+                                            double* errors_out, void* blob, size_t blob_bytes, int blob_on_device,
+                                            hipStream_t stream, svdq_layer* out) {
+  svdq_status st = check_common(K, N, rank_capacity, fmt, dtype);
+  if (st != SVDQ_OK) return st;
+  if (!blob || !out) return SVDQ_ERR_INVALID_ARG;
+  size_t need = blob_offsets(K, N, slots_for(rank_capacity), fmt).total;
+  if (blob_bytes < need) return SVDQ_ERR_CAPACITY;
+  if (!blob_on_device)
+    return pack_host(W_host, K, N, ldw, dtype, act_absmax_host, rank, rank_capacity, fmt, bias_host,
+                     static_cast<uint8_t*>(blob), blob_bytes, out, 0, blob, refine_iters, errors_out);
+  std::vector<uint8_t> host(need);
+  st = pack_host(W_host, K, N, ldw, dtype, act_absmax_host, rank, rank_capacity, fmt, bias_host, host.data(),
+                 need, out, 1, blob, refine_iters, errors_out);
+  if (st != SVDQ_OK) return st;
+  out->blob_bytes = blob_bytes;
+  return copy_bytes(blob, 1, host.data(), 0, need, stream);
 }
 
 extern "C" svdq_status svdq_layer_copy(const svdq_layer* src, void* dst, size_t dst_bytes, int dst_on_device,

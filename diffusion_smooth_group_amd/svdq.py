@@ -60,6 +60,7 @@ _SIGS = {
     "svdq_packed_size": [_I64, _I64, _I, _I, _I, C.POINTER(_SZ)],
     "svdq_pack_weights": [_P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _P, _P, _SZ, _P, _LP],
     "svdq_pack_weights_host": [_P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _P, _P, _SZ, _LP],
+    "svdq_pack_weights_ex": [_P, _I64, _I64, _I64, _I, _P, _I, _I, _I, _P, _I, _P, _P, _SZ, _I, _P, _LP],
     "svdq_layer_copy": [_LP, _P, _SZ, _I, _P, _LP],
     "svdq_attach_lora": [_LP, _P, _P, _I, C.c_float, _P],
     "svdq_detach_lora": [_LP, _P],
@@ -131,9 +132,11 @@ def packed_size(K, N, rank_capacity, fmt, dtype) -> int:
 
 
 def pack_weights_host(W_bits: np.ndarray, dtype: int, act_absmax: Optional[np.ndarray], rank: int,
-                      rank_capacity: int, fmt: int, bias_bits: Optional[np.ndarray] = None):
+                      rank_capacity: int, fmt: int, bias_bits: Optional[np.ndarray] = None, refine_iters: int = 0,
+                      errors: Optional[np.ndarray] = None):
     """Pack into a host blob.  Returns (layer, blob ndarray); the blob must
-    outlive the layer."""
+    outlive the layer.  refine_iters > 0 refines the low-rank split; errors
+    (float64 [refine_iters + 1]) receives each round's squared weight error."""
     W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
     K, N = W_bits.shape
     a = None if act_absmax is None else np.ascontiguousarray(act_absmax, dtype=np.float32)
@@ -141,8 +144,13 @@ def pack_weights_host(W_bits: np.ndarray, dtype: int, act_absmax: Optional[np.nd
     nbytes = packed_size(K, N, rank_capacity, fmt, dtype)
     blob = np.zeros(nbytes, np.uint8)
     L = svdq_layer()
-    _call("svdq_pack_weights_host", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, rank_capacity, fmt,
-          _np_ptr(b), _np_ptr(blob), nbytes, C.byref(L))
+    if refine_iters == 0 and errors is None:
+        _call("svdq_pack_weights_host", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, rank_capacity, fmt,
+              _np_ptr(b), _np_ptr(blob), nbytes, C.byref(L))
+    else:
+        assert errors is None or (errors.dtype == np.float64 and errors.size >= refine_iters + 1)
+        _call("svdq_pack_weights_ex", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, rank_capacity, fmt,
+              _np_ptr(b), refine_iters, _np_ptr(errors), _np_ptr(blob), nbytes, 0, None, C.byref(L))
     return L, blob
 
 
@@ -231,7 +239,10 @@ class SVDQLinear:
     @classmethod
     def pack(cls, W_bits: np.ndarray, dtype: int, act_absmax: Optional[np.ndarray], rank: int, fmt: int,
              bias_bits: Optional[np.ndarray] = None, rank_capacity: Optional[int] = None, device="cuda",
-             stream=None):
+             stream=None, refine_iters: int = 0):
+        """refine_iters > 0: iterative refinement of the low-rank split (the
+        split with the smallest weight error is packed; the squared errors of
+        every round land in .refine_errors)."""
         import torch
         W_bits = np.ascontiguousarray(W_bits, dtype=np.uint16)
         K, N = W_bits.shape
@@ -241,9 +252,17 @@ class SVDQLinear:
         a = None if act_absmax is None else np.ascontiguousarray(act_absmax, dtype=np.float32)
         b = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
         L = svdq_layer()
-        _call("svdq_pack_weights", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, cap, fmt, _np_ptr(b),
-              _t_ptr(blob), nbytes, _stream(stream), C.byref(L))
-        return cls(L, blob)
+        if refine_iters == 0:
+            _call("svdq_pack_weights", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, cap, fmt, _np_ptr(b),
+                  _t_ptr(blob), nbytes, _stream(stream), C.byref(L))
+            errors = None
+        else:
+            errors = np.zeros(refine_iters + 1, np.float64)
+            _call("svdq_pack_weights_ex", _np_ptr(W_bits), K, N, N, dtype, _np_ptr(a), rank, cap, fmt, _np_ptr(b),
+                  refine_iters, _np_ptr(errors), _t_ptr(blob), nbytes, 1, _stream(stream), C.byref(L))
+        lin = cls(L, blob)
+        lin.refine_errors = errors
+        return lin
 
     @property
     def K(self):

@@ -119,6 +119,24 @@ svdq_status svdq_pack_weights_host(const void* W_host, int64_t K, int64_t N, int
                                    const float* act_absmax_host, int rank, int rank_capacity, svdq_format fmt,
                                    const void* bias_host, void* blob_host, size_t blob_bytes, svdq_layer* out);
 
+/* svdq_pack_weights with iterative refinement of the low-rank split
+ * [SVDQuant §4.2, the closing remark on the low-rank branch]: after the
+ * one-shot split, each of refine_iters rounds splits W_hat - deq(Q(R)) at
+ * rank `rank` again (deq(Q(R)): the previous round's quantized residual),
+ * rounds the factors to 16 bits, re-derives R and its codes, and measures
+ * err = ||W_hat - diag(lambda) L1x L2 - deq(Q(R))||_F^2 (float64).  The split
+ * with the smallest err is packed.  0 <= refine_iters <=
+ * SVDQ_MAX_REFINE_ITERS; refine_iters = 0 packs exactly what
+ * svdq_pack_weights packs.  errors_out: NULL or [refine_iters + 1] doubles,
+ * err of the one-shot split first.  blob_on_device: 1 = blob is device
+ * memory (copied on `stream`), 0 = host memory.  Synchronous; each round
+ * costs about one pack. */
+#define SVDQ_MAX_REFINE_ITERS 16
+svdq_status svdq_pack_weights_ex(const void* W_host, int64_t K, int64_t N, int64_t ldw, svdq_dtype dtype,
+                                 const float* act_absmax_host, int rank, int rank_capacity, svdq_format fmt,
+                                 const void* bias_host, int refine_iters, double* errors_out, void* blob,
+                                 size_t blob_bytes, int blob_on_device, hipStream_t stream, svdq_layer* out);
+
 /* Copy a packed layer's blob (host or device) to another buffer (host or
  * device) and describe the copy in `out` (restore / upload).  dst_on_device
  * selects the destination kind.  Synchronous on `stream`. */

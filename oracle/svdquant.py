@@ -49,6 +49,7 @@ __all__ = [
     "output_epilogue_f64",
     "pack", "pack_from_factors", "attach_lora", "forward", "forward_fp32_timed",
     "quantization_error", "prop41_bound", "lowrank_overhead", "packed_bytes",
+    "split_error", "refine_split",
 ]
 
 
@@ -430,6 +431,48 @@ def pack(W_bits, dtype, act_absmax, r: int, fmt: str, bias_bits=None) -> Dict[st
         "L1x": L1x, "L2q": L2q, "R": pf["R"], "qw": pf["qw"], "sw": pf["sw"],
         "bias": None if bias_bits is None else np.asarray(bias_bits, dtype=np.uint16),
     }
+
+
+# ---------------------------------------------------------------------------
+# O10  iterative refinement of the low-rank split  [SVDQuant §4.2, closing
+#      remark on the low-rank branch: decompose again with the quantized
+#      residual taken out, adjust the residual, repeat, keep the smallest
+#      error]
+# ---------------------------------------------------------------------------
+def split_error(W_bits, dtype, lam, L1x_bits, L2q_bits, qw, sw, fmt) -> float:
+    """err = ||W_hat - diag(lambda) L1x L2q - deq(Q(R))||_F^2 in float64: how
+    far the packed layer (16-bit low-rank branch plus dequantized residual)
+    is from the smoothed weight.  Reading: the pages name "the error" without
+    a formula; the weight-space Frobenius error is the quantity the split
+    itself minimises."""
+    W = decode16(W_bits, dtype)
+    What = smoothed_weight(W, lam)
+    lam64 = np.asarray(lam, dtype=np.float64)
+    lr = lam64[:, None] * (decode16(L1x_bits, dtype) @ decode16(L2q_bits, dtype))
+    D = What - lr - dequant_weight(qw, sw, fmt)
+    return float(np.sum(D * D))
+
+
+def refine_split(W_bits, dtype, act_absmax, r: int, fmt: str, iters: int) -> Dict[str, object]:
+    """Round 0 is the one-shot split of W_hat.  Round i >= 1 splits
+    B_i = W_hat - deq(Q(R_{i-1})) at rank r (B_i's truncated SVD), rounds the
+    factors to 16 bits, re-derives R_i = fl32(W_hat - diag(lambda) L1x L2q)
+    and its codes.  Returns every round's (L1x, L2q, qw, sw, err) and the index
+    of the smallest err."""
+    W = decode16(W_bits, dtype)
+    lam, invlam = smoothing_factors(act_absmax, weight_channel_absmax(W))
+    What = smoothed_weight(W, lam)
+    rounds = []
+    B = What
+    for i in range(int(iters) + 1):
+        L1, L2, _ = truncated_svd(B, r)
+        L1x, L2q = runtime_factors(L1, L2, invlam, dtype)
+        pf = pack_from_factors(W_bits, dtype, lam, L1x, L2q, fmt)
+        err = split_error(W_bits, dtype, lam, L1x, L2q, pf["qw"], pf["sw"], fmt)
+        rounds.append({"L1x": L1x, "L2q": L2q, "qw": pf["qw"], "sw": pf["sw"], "err": err})
+        B = What - dequant_weight(pf["qw"], pf["sw"], fmt)
+    best = int(np.argmin([x["err"] for x in rounds]))
+    return {"lam": lam, "invlam": invlam, "rounds": rounds, "best": best}
 
 
 def attach_lora(layer: Dict[str, object], A_bits, B_bits, alpha: float = 1.0) -> Dict[str, object]:

@@ -32,9 +32,10 @@ def calib_absmax_gpu(Xd, dtype):
     return a.cpu().numpy()
 
 
-def pack_gpu(d, fmt, rank, cap=None, absmax=None):
+def pack_gpu(d, fmt, rank, cap=None, absmax=None, refine=0):
     dt = d["dtype"]
-    lin = S.SVDQLinear.pack(d["W"], DTS[dt], absmax, rank, FMTS[fmt], d["bias"], rank_capacity=cap)
+    lin = S.SVDQLinear.pack(d["W"], DTS[dt], absmax, rank, FMTS[fmt], d["bias"], rank_capacity=cap,
+                            refine_iters=refine)
     return lin
 
 
@@ -63,7 +64,7 @@ def compare_outputs(Y_gpu_bits, Y_ref_bits, dtype, what=""):
 
 
 def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, cap=None, alpha=1.0,
-                   check_codes=True, unfused=False):
+                   check_codes=True, unfused=False, refine=0):
     """Pack on the GPU, run the forward, and compare with the oracle.
     rows / cols: sample of outputs evaluated by the oracle (None = all)."""
     import torch
@@ -75,7 +76,7 @@ def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, c
     ref_absmax = o.activation_absmax(o.decode16(d["X"], dt))
     assert np.array_equal(absmax.view(np.uint32), ref_absmax.view(np.uint32)), "calibration absmax"
     lin = pack_gpu(d, fmt, rank, cap=cap if cap is not None else (rank + (d["lora_A"].shape[1] if lora else 0)),
-                   absmax=absmax)
+                   absmax=absmax, refine=refine)
     if lora:
         lin.attach_lora(d["lora_A"], d["lora_B"], alpha)
     Y = lin.forward(Xd, gelu=gelu, unfused=unfused)

@@ -71,6 +71,16 @@ def test_unfused_lowrank_qkv_sampled():
     G.run_layer_case(d5, o.MXFP4, 32, lora=True, rows=rows, cols=cols, unfused=True)
 
 
+@pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
+def test_refined_pack_forward(fmt):
+    # a pack whose low-rank split was refined (device blob written through
+    # svdq_pack_weights_ex) meets the same gates
+    d = _small(130, 512, 384, o.BF16, fmt, 16, lora=16, seed=80)
+    lin, _ = G.run_layer_case(d, fmt, 16, lora=True, gelu=True, refine=2)
+    e = lin.refine_errors
+    assert e is not None and e.shape == (3,) and np.all(np.isfinite(e)) and e.min() <= e[0]
+
+
 @pytest.mark.parametrize("M", [1, 17, 256, 300])
 def test_token_counts(M):
     d = _small(M, 256, 128, o.F16, o.INT4, 8, seed=3 + M)

@@ -203,3 +203,47 @@ def test_config1_full_pack_matches_oracle():
     What = o.smoothed_weight(o.decode16(d["W"], o.F16), ref["lam"])
     L1, L2, sg, _ = S.svd_factors(d["W"], S.F16, a, 32)
     assert abs(np.linalg.norm(What - L1 @ L2, 2) / ref["sigma"][32] - 1) < 1e-6
+
+
+# ------------------------------------------------ low-rank split refinement
+@pytest.mark.parametrize("fmt", [o.INT4, o.MXFP4])
+def test_refined_pack_against_oracle(fmt):
+    K, N, dt, r = 256, 384, o.BF16, 16
+    d = _inputs(K=K, N=N, dtype=dt, seed=70, w_out=3)
+    a = o.activation_absmax(o.decode16(d["X"], dt))
+    # zero rounds: byte for byte the plain pack, and its error is the oracle's
+    L0, b0 = S.pack_weights_host(d["W"], DTS[dt], a, r, 32, FMTS[fmt], d["bias"])
+    e0 = np.zeros(1, np.float64)
+    L1, b1 = S.pack_weights_host(d["W"], DTS[dt], a, r, 32, FMTS[fmt], d["bias"], refine_iters=0, errors=e0)
+    assert np.array_equal(b0, b1)
+    ex = S.layer_export(L1)
+    ref0 = o.split_error(d["W"], dt, ex["lam"], ex["L1x"], ex["L2q"], ex["codes"], ex["scales"], fmt)
+    assert abs(e0[0] - ref0) <= 1e-9 * ref0
+    # three rounds: the packed split is the one with the smallest reported
+    # error, its codes follow from its factors, and its error is the oracle's
+    it = 3
+    errs = np.zeros(it + 1, np.float64)
+    L3, b3 = S.pack_weights_host(d["W"], DTS[dt], a, r, 32, FMTS[fmt], d["bias"], refine_iters=it, errors=errs)
+    ex3 = S.layer_export(L3)
+    pf = o.pack_from_factors(d["W"], dt, ex3["lam"], ex3["L1x"], ex3["L2q"], fmt)
+    assert np.array_equal(ex3["codes"].astype(np.int64), pf["qw"].astype(np.int64))
+    assert np.array_equal(ex3["scales"], pf["sw"])
+    ref3 = o.split_error(d["W"], dt, ex3["lam"], ex3["L1x"], ex3["L2q"], ex3["codes"], ex3["scales"], fmt)
+    assert abs(errs.min() - ref3) <= 1e-9 * ref3
+    assert abs(errs[0] - ref0) <= 1e-9 * ref0
+    assert errs.min() < errs[0]
+    # the oracle's own refinement (LAPACK SVD) follows the same trajectory
+    # up to the SVDs' last bits: same one-shot error, best error within 2%
+    orc = o.refine_split(d["W"], dt, a, r, fmt, it)
+    oerr = [x["err"] for x in orc["rounds"]]
+    assert abs(oerr[0] - errs[0]) <= 1e-3 * oerr[0]
+    assert abs(min(oerr) - errs.min()) <= 2e-2 * min(oerr)
+
+
+def test_refine_iters_bounds():
+    d = _inputs()
+    a = o.activation_absmax(o.decode16(d["X"], o.BF16))
+    for bad in (-1, 17):
+        with pytest.raises(S.SvdqError) as e:
+            S.pack_weights_host(d["W"], S.BF16, a, 8, 8, S.FMT_INT4_G64, refine_iters=bad)
+        assert e.value.code == 1
