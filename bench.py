@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--lowrank-study", action="store_true",
                     help="instead of the headline line, time the forward three ways -- W4A4 only (rank 0), "
                          "fused low-rank branch, low-rank branch as separate passes -- and print their overheads")
+    ap.add_argument("--chain-study", action="store_true",
+                    help="instead of the headline line, time the FLUX MLP pair (fc1 + GELU -> fc2, MXFP4) with "
+                         "fc2's activation pass as its own kernel and chained into fc1's GEMM epilogue")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, time a plain device copy of MIB MiB (the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -218,6 +221,99 @@ def lowrank_study(args):
         "runs_us": {k: [round(x, 2) for x in v] for k, v in runs.items()}}), flush=True)
 
 
+def chain_study(args):
+    """The MLP pair fc1 (+GELU) -> fc2 two ways: unchained (fc1 writes Y1,
+    fc2's activation kernel reads it back) and chained (fc2's codes, scales
+    and down-projection come out of fc1's GEMM epilogue; Y1 is not stored)."""
+    import ctypes as C
+    import torch
+    from diffusion_smooth_group_amd import svdq as S
+    from diffusion_smooth_group_amd import workloads as wl
+    fc1, fc2 = wl.config_shapes(3)
+    M, K, H = fc1.M, fc1.K, fc1.N
+    dt, fmt = S.BF16, S.FMT_MXFP4_G32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d1 = wl.generate(fc1)
+    d2 = wl.generate(fc2, fc1_inputs=d1)
+    lins = []
+    for d in (d1, d2):
+        am = S.activation_absmax(S.bits_to_device(d["X"], dt, dev), dt)
+        torch.cuda.synchronize()
+        lins.append(S.SVDQLinear.pack(d["W"], dt, am.cpu().numpy(), args.rank, fmt, d["bias"],
+                                      rank_capacity=args.rank))
+    lib = S.lib_handle()
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+    nrot = max(1, args.rotate)
+    X0 = S.bits_to_device(d1["X"], dt, dev)
+    sets = []
+    for r in range(nrot):
+        L = []
+        blobs = []
+        for lin in lins:
+            if r == 0:
+                L.append(lin.layer)
+                continue
+            b = torch.empty_like(lin.blob)
+            L.append(S.layer_copy(lin.layer, S._t_ptr(b), b.numel(), True))
+            blobs.append(b)
+        cw = C.c_size_t()
+        lib.svdq_chain_workspace_size(C.byref(L[0]), C.byref(L[1]), M, C.byref(cw))
+        sets.append({"L": L, "blobs": blobs, "X": X0 if r == 0 else X0.clone(),
+                     "Y1": torch.empty((M, H), dtype=X0.dtype, device=dev),
+                     "Y2": torch.empty((M, K), dtype=X0.dtype, device=dev),
+                     "ws1": torch.empty(cw.value, dtype=torch.uint8, device=dev), "ws1b": cw.value,
+                     "ws2": torch.empty(S.workspace_size(L[1], M), dtype=torch.uint8, device=dev),
+                     "ws2b": S.workspace_size(L[1], M)})
+
+    def check(rc, fn):
+        if rc != 0:
+            raise S.SvdqError(fn, rc)
+
+    def unchained(i):
+        z = sets[i % nrot]
+        check(lib.svdq_linear_forward(C.byref(z["L"][0]), S._t_ptr(z["X"]), M, K, S._t_ptr(z["Y1"]), H,
+                                      S._t_ptr(z["ws1"]), z["ws1b"], S.FLAG_GELU, sh), "svdq_linear_forward")
+        check(lib.svdq_linear_forward(C.byref(z["L"][1]), S._t_ptr(z["Y1"]), M, H, S._t_ptr(z["Y2"]), K,
+                                      S._t_ptr(z["ws2"]), z["ws2b"], 0, sh), "svdq_linear_forward")
+
+    def chained(i):
+        z = sets[i % nrot]
+        check(lib.svdq_linear_forward_chain(C.byref(z["L"][0]), C.byref(z["L"][1]), S._t_ptr(z["X"]), M, K, None, 0,
+                                            S._t_ptr(z["ws1"]), z["ws1b"], S._t_ptr(z["ws2"]), z["ws2b"],
+                                            S.FLAG_GELU, sh), "svdq_linear_forward_chain")
+        check(lib.svdq_gemm_forward(C.byref(z["L"][1]), M, S._t_ptr(z["Y2"]), K, S._t_ptr(z["ws2"]), z["ws2b"], 0,
+                                    sh), "svdq_gemm_forward")
+
+    def timed(fn):
+        for i in range(args.warmup):
+            fn(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(args.steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps
+
+    runs = {"unchained": [], "chained": []}
+    for _ in range(3):              # interleaved rounds, medians reported
+        runs["unchained"].append(timed(unchained))
+        runs["chained"].append(timed(chained))
+    tu, tc = (float(np.median(runs[k])) for k in ("unchained", "chained"))
+    flops = 2.0 * M * K * H * 2
+    print(json.dumps({
+        "study": "MLP pair fc1 (+GELU) -> fc2: fc2's activation pass as its own kernel vs chained into fc1's epilogue",
+        "workload": f"flux_mlp_{M}x{K}x{H}x{K}", "format": "mxfp4_g32", "rank": args.rank, "activation_dtype": "bf16",
+        "rotating_buffer_sets": nrot, "steps": args.steps, "rounds": 3,
+        "t_unchained_us": round(tu, 2), "t_chained_us": round(tc, 2),
+        "saving_pct": round(100.0 * (tu - tc) / tu, 1),
+        "pair_tops_unchained": round(flops / tu * 1e-6, 1), "pair_tops_chained": round(flops / tc * 1e-6, 1),
+        "runs_us": {k: [round(x, 2) for x in v] for k, v in runs.items()}}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -229,6 +325,9 @@ def main():
         return
     if args.lowrank_study:
         lowrank_study(args)
+        return
+    if args.chain_study:
+        chain_study(args)
         return
     import torch
     from diffusion_smooth_group_amd import svdq as S

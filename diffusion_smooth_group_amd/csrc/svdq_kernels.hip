@@ -625,6 +625,19 @@ struct MxParams {
   // and of the token-side regions from xq (all in the workspace); both spans
   // are below 2 GiB, so the stage loads take them as scalar offsets
   int off_wq, off_sw, off_sx, off_t;
+  // Epilogue chaining (CHAIN): this layer's output is the next layer's
+  // input.  nx_invlam: the next layer's 1/lambda over this layer's N
+  // columns; nx_l1x: its L1x in the activation kernel's tiling; nx_xq,
+  // nx_sx: its workspace codes and scales (written here); nx_tp: fp32
+  // partial down-projections [tiles_n][nx_Mp][nx_slots], one slab per
+  // 256-column tile of this layer (summed by k_tfin).
+  const float* nx_invlam;
+  const uint16_t* nx_l1x;
+  uint8_t* nx_xq;
+  uint8_t* nx_sx;
+  float* nx_tp;
+  int64_t nx_Mp;
+  int nx_slots, nx_njt;
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -656,7 +669,107 @@ __device__ __forceinline__ f32x16 mfma32x16(u32x4 a, u32x4 b, f32x16 c) {
 
 
 
-template <int DT, bool GELU>
+// Epilogue chaining: the staged 16-bit output tile (the exact bits the
+// layer would store) is the next layer's input, so its activation kernel
+// pass is done here.  Per wave (128 tokens x 128 columns = one 128-deep K
+// step of the next layer):
+//  * codes and scales: lane l takes token 32t + l % 32 and block
+//    b = 2h + l / 32 of the step -- exactly one 16-byte piece of the next
+//    layer's fragment and one byte of its scale dword -- and applies the
+//    activation kernel's rule (x_hat = x * invlambda in fp32, e8m0 of the
+//    block absmax, E2M1 codes);
+//  * down-projection: after a workgroup barrier, wave (wm, wn) sums
+//    x L1x over all 256 columns of the tile (its own and its neighbour's
+//    staged halves) for tokens 64 wn .. 64 wn + 63 of the pair's 128, on
+//    the 16 x 16 x 32 MFMA with L1x as the A operand, and writes the fp32
+//    result to this column tile's slab.
+template <int DT>
+__device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t* smem, const uint8_t* ob, int wave,
+                                               int lane, int64_t m0, int64_t n0, int64_t nw, int64_t mw) {
+  const int wn = wave & 1, wm = wave >> 1;
+  const int nst = int(p.N / KSTEP);        // K steps of the next layer
+  if (nw < p.N) {
+    const int s2 = int(nw / KSTEP), half = lane >> 5, r32 = lane & 31;
+    unsigned sdw[2] = {0u, 0u};            // scale dwords of the two 32-tile pairs
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int b = 2 * h + half;
+      f32x4 il[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) il[e] = *reinterpret_cast<const f32x4*>(p.nx_invlam + nw + 32 * b + 4 * e);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint8_t* src = ob + (32 * t + r32) * mx::OUT_PITCH + 64 * b;
+        float xh[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * i);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int x = 8 * i + 2 * e;
+            xh[x] = h2f<DT>(v[e] & 0xFFFFu) * il[x >> 2][x & 3];
+            xh[x + 1] = h2f<DT>(v[e] >> 16) * il[(x + 1) >> 2][(x + 1) & 3];
+          }
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int x = 0; x < 32; ++x) am = fmaxf(am, fabsf(xh[x]));
+        const int ex = e8m0_needs_slow(am) ? e8m0_slow(am) : e8m0_fast(am);
+        const float scl = ex != 0 ? __uint_as_float(unsigned(ex) << 23) : 1.0f;
+        unsigned d[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          unsigned v = 0u;
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) {
+            const unsigned cv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xh[8 * i + 2 * bb], xh[8 * i + 2 * bb + 1], scl, 0);
+            v |= (cv & 0xFFu) << (8 * bb);
+          }
+          d[i] = v;
+        }
+        const int64_t tg = mw / 32 + t;
+        *reinterpret_cast<u32x4*>(p.nx_xq + ((size_t(tg) * nst + s2) * 2 + h) * 1024 + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
+        sdw[t >> 1] |= unsigned(ex) << (8 * (2 * (t & 1) + h));
+      }
+    }
+#pragma unroll
+    for (int tp = 0; tp < 2; ++tp)
+      reinterpret_cast<unsigned*>(p.nx_sx)[(size_t(mw / 64 + tp) * nst + s2) * 64 + lane] = sdw[tp];
+  }
+  if (p.nx_njt == 0) return;               // uniform over the workgroup
+  __syncthreads();                         // both halves of the pair are staged
+  const int cs = p.nx_slots / 16;
+  const int nblk = n0 + 128 < p.N ? 2 : 1; // column halves of the tile inside N
+  const u32x4* l1x = reinterpret_cast<const u32x4*>(p.nx_l1x);
+  float* tp = p.nx_tp + (size_t(n0 / 256) * p.nx_Mp + mw + 64 * wn) * p.nx_slots;
+  const int q = lane >> 4;
+  for (int jt = 0; jt < p.nx_njt; ++jt) {
+    u32x4 la[2][4];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        la[x][c] = x < nblk ? l1x[((size_t(n0 / KSTEP + x) * cs + jt) * 4 + c) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 64 * wn + 16 * u + (lane & 15);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        if (x < nblk) {
+          const uint8_t* src = smem + (2 * wm + x) * (128 * mx::OUT_PITCH) + row * mx::OUT_PITCH + 16 * q;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc = mfma16<DT>(la[x][c], *reinterpret_cast<const u32x4*>(src + 64 * c), acc);
+        }
+      }
+      // lane holds T[token row][16 jt + 4 q + i]
+      *reinterpret_cast<f32x4*>(tp + size_t(16 * u + (lane & 15)) * p.nx_slots + 16 * jt + 4 * q) = acc;
+    }
+  }
+}
+
+template <int DT, bool GELU, bool CHAIN = false>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   // one LDS object (a second one makes the compiler wait for every global->LDS
   // load before any LDS read)
@@ -945,8 +1058,8 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       }
     }
     SVDQ_WAIT_LGKM0();
-    if (nw < p.N) {
-      const int64_t mw = m0 + 128 * wm;
+    const int64_t mw = m0 + 128 * wm;      // first token of this wave's tile
+    if (nw < p.N && (!CHAIN || p.Y != nullptr)) {
 #pragma unroll 4
       for (int it = 0; it < 32; ++it) {
         const int row = 4 * it + (lane >> 4);
@@ -955,6 +1068,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         if (mw + row < p.M) *reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col) = val;
       }
     }
+    if constexpr (CHAIN) chain_epilogue<DT>(p, smem, ob, wave, lane, m0, n0, nw, mw);
   }
 }
 
@@ -1057,6 +1171,37 @@ __global__ __launch_bounds__(256) void k_up(UpParams p) {
 }
 
 // -------------------------------------------------- INT4 per-group products
+// Finishes a chained down-projection: T[m][j] = round16(sum over the
+// column-tile slabs of the fp32 partials, in slab order), written in the
+// GEMM's low-rank operand layout.  One thread = one token x 8 consecutive
+// ranks (16 contiguous bytes in that layout).
+struct TfinParams {
+  const float* tp;       // [nparts][Mp][slots]
+  uint16_t* t;
+  int64_t Mp;
+  int slots, nparts, ncols8;
+};
+
+template <int DT>
+__global__ __launch_bounds__(64) void k_tfin(TfinParams p) {
+  const int64_t g = int64_t(blockIdx.x) * 64 + threadIdx.x;
+  const int64_t m = g / p.ncols8;
+  const int j8 = int(g % p.ncols8);
+  if (m >= p.Mp) return;
+  const float* src = p.tp + m * p.slots + 8 * j8;
+  const size_t stride = size_t(p.Mp) * size_t(p.slots);
+  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+  for (int q = 0; q < p.nparts; ++q) {
+    s0 += *reinterpret_cast<const f32x4*>(src + q * stride);
+    s1 += *reinterpret_cast<const f32x4*>(src + q * stride + 4);
+  }
+  // MXFP4 low-rank layout: 32-row tiles, 16-rank chunks, lane (row % 32) + 32 (j % 16 >= 8)
+  const int64_t t = m / 32, c = j8 / 2;
+  const int64_t ln = (m % 32) + 32 * (j8 % 2);
+  *reinterpret_cast<u32x4*>(p.t + ((t * (p.slots / 16) + c) * 64 + ln) * 8) =
+      u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]), pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
+}
+
 struct PartialParams {
   const uint8_t* wq;
   const uint8_t* xq;
@@ -1142,9 +1287,8 @@ void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   else hipLaunchKernelGGL((k2_int4<DT, false>), grid, dim3(256), 0, st, kp);
 }
 
-template <int DT>
-void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
-  MxParams mp;
+MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
+  MxParams mp = {};
   mp.wq = kp.wq; mp.sw = kp.sw; mp.l2 = kp.l2; mp.bias = kp.bias; mp.xq = kp.xq; mp.sx = kp.sx; mp.t = kp.t;
   mp.Y = kp.Y; mp.ldy = kp.ldy; mp.M = kp.M; mp.N = kp.N; mp.K = kp.K; mp.slots = kp.slots;
   mp.nchunks16 = kp.nchunks16;
@@ -1154,9 +1298,22 @@ void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipSt
   mp.off_sw = int(kp.sw - reinterpret_cast<const uint8_t*>(kp.l2));
   mp.off_sx = int(kp.sx - kp.xq);
   mp.off_t = int(reinterpret_cast<const uint8_t*>(kp.t) - kp.xq);
+  return mp;
+}
+
+template <int DT>
+void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+  const MxParams mp = mx_params(kp, w);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
   if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), dim3(T), dim3(256), 0, st, mp);
   else hipLaunchKernelGGL((k2_mx<DT, false>), dim3(T), dim3(256), 0, st, mp);
+}
+
+template <int DT>
+void launch_k2_mx_chain(const MxParams& mp, bool gelu, hipStream_t st) {
+  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, true>), dim3(T), dim3(256), 0, st, mp);
+  else hipLaunchKernelGGL((k2_mx<DT, false, true>), dim3(T), dim3(256), 0, st, mp);
 }
 
 template <int DT, int FMT>
@@ -1215,9 +1372,8 @@ void run_k1(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx, uint
   }
 }
 
-// K2 on checked arguments; lowrank = false leaves the low-rank branch out
-void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
-            bool gelu, bool lowrank, hipStream_t stream) {
+K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws,
+                   const svdq::WsOffsets& w, bool lowrank) {
   const uint8_t* blob = static_cast<const uint8_t*>(L->blob);
   K2Params kp;
   kp.wq = blob + L->off_wq;
@@ -1232,6 +1388,13 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
   const int ra = lowrank ? L->rank_active : 0;
   kp.nchunks = int(svdq::ceil_div(ra, 32));
   kp.nchunks16 = int(svdq::ceil_div(ra, 16));
+  return kp;
+}
+
+// K2 on checked arguments; lowrank = false leaves the low-rank branch out
+void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
+            bool gelu, bool lowrank, hipStream_t stream) {
+  const K2Params kp = k2_params(L, M, Y_dev, ldy, ws, w, lowrank);
   if (L->fmt == SVDQ_FMT_INT4_G64) {
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
     else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
@@ -1290,7 +1453,81 @@ svdq_status check_ws(const svdq_layer* L, int64_t M, const void* ws_dev, size_t 
   return SVDQ_OK;
 }
 
+// Epilogue chaining: `first` feeds `next` (same dtype, MXFP4 both,
+// first->N == next->K).  The fp32 partial down-projections of `next` sit
+// after `first`'s own workspace.
+svdq_status check_chain(const svdq_layer* A, const svdq_layer* B) {
+  svdq_status st = check_device_layer(A);
+  if (st != SVDQ_OK || (st = check_device_layer(B)) != SVDQ_OK) return st;
+  if (A->dtype != B->dtype) return SVDQ_ERR_INVALID_ARG;
+  if (A->N != B->K) return SVDQ_ERR_SHAPE;
+  if (A->fmt != SVDQ_FMT_MXFP4_G32 || B->fmt != SVDQ_FMT_MXFP4_G32) return SVDQ_ERR_UNSUPPORTED;
+  return SVDQ_OK;
+}
+size_t chain_partials_offset(const svdq::WsOffsets& w) { return svdq::align256(w.total); }
+size_t chain_partials_bytes(const svdq_layer* A, const svdq_layer* B, const svdq::WsOffsets& w) {
+  return size_t(svdq::ceil_div(A->N, 256)) * size_t(w.Mp) * size_t(B->rank_slots) * 4;
+}
+
 }  // namespace
+
+extern "C" svdq_status svdq_chain_workspace_size(const svdq_layer* first, const svdq_layer* next, int64_t M,
+                                                 size_t* bytes) {
+  svdq_status st = check_chain(first, next);
+  if (st != SVDQ_OK) return st;
+  if (M < 0 || !bytes) return SVDQ_ERR_INVALID_ARG;
+  const svdq::WsOffsets w = svdq::ws_offsets(M, first->K, first->rank_slots, first->fmt);
+  *bytes = chain_partials_offset(w) + chain_partials_bytes(first, next, w);
+  return SVDQ_OK;
+}
+
+extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const svdq_layer* next, const void* X_dev,
+                                                 int64_t M, int64_t ldx, void* Y_dev, int64_t ldy, void* ws_dev,
+                                                 size_t ws_bytes, void* ws_next_dev, size_t ws_next_bytes,
+                                                 unsigned flags, hipStream_t stream) {
+  svdq_status st = check_chain(first, next);
+  if (st != SVDQ_OK) return st;
+  if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
+  if (M == 0) return SVDQ_OK;
+  svdq::WsOffsets w, wn;
+  if ((st = check_x(first, X_dev, ldx)) != SVDQ_OK || (st = check_ws(next, M, ws_next_dev, ws_next_bytes, &wn)) != SVDQ_OK)
+    return st;
+  if (Y_dev && (st = check_y(first, Y_dev, ldy)) != SVDQ_OK) return st;
+  if (!ws_dev) return SVDQ_ERR_INVALID_ARG;
+  w = svdq::ws_offsets(M, first->K, first->rank_slots, first->fmt);
+  if (ws_bytes < chain_partials_offset(w) + chain_partials_bytes(first, next, w)) return SVDQ_ERR_CAPACITY;
+  if (!aligned(ws_dev, 256)) return SVDQ_ERR_INVALID_ARG;
+  if (!mx_offsets_fit(first, w)) return SVDQ_ERR_UNSUPPORTED;
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  uint8_t* wsn = static_cast<uint8_t*>(ws_next_dev);
+  const uint8_t* nblob = static_cast<const uint8_t*>(next->blob);
+  run_k1(first, X_dev, M, ldx, ws, w, K1_BOTH, stream);
+  MxParams mp = mx_params(k2_params(first, M, Y_dev, ldy, ws, w, true), w);
+  mp.nx_invlam = reinterpret_cast<const float*>(nblob + next->off_invlam);
+  mp.nx_l1x = reinterpret_cast<const uint16_t*>(nblob + next->off_l1x);
+  mp.nx_xq = wsn + wn.xq;
+  mp.nx_sx = wsn + wn.sx;
+  mp.nx_tp = reinterpret_cast<float*>(ws + chain_partials_offset(w));
+  mp.nx_Mp = w.Mp;
+  mp.nx_slots = next->rank_slots;
+  mp.nx_njt = int(svdq::ceil_div(next->rank_active, 16));
+  const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
+  if (first->dtype == SVDQ_BF16) launch_k2_mx_chain<SVDQ_BF16>(mp, gelu, stream);
+  else launch_k2_mx_chain<SVDQ_F16>(mp, gelu, stream);
+  if (mp.nx_njt > 0) {
+    TfinParams tf;
+    tf.tp = mp.nx_tp;
+    tf.t = reinterpret_cast<uint16_t*>(wsn + wn.t);
+    tf.Mp = w.Mp;
+    tf.slots = next->rank_slots;
+    tf.nparts = mp.tiles_n;
+    tf.ncols8 = 2 * mp.nx_njt;
+    const int64_t n = w.Mp * tf.ncols8;
+    if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16>), dim3(unsigned((n + 63) / 64)), dim3(64), 0, stream, tf);
+    else hipLaunchKernelGGL((k_tfin<SVDQ_F16>), dim3(unsigned((n + 63) / 64)), dim3(64), 0, stream, tf);
+  }
+  return launch_ok();
+}
 
 extern "C" svdq_status svdq_quantize_activations(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx,
                                                  void* ws_dev, size_t ws_bytes, hipStream_t stream) {

@@ -72,6 +72,8 @@ _SIGS = {
     "svdq_layer_export": [_LP, _P, _P, _P, _P, _P, _P, _P, _P],
     "svdq_workspace_export": [_LP, _P, _SZ, _I64, _P, _P, _P, _P],
     "svdq_svd_factors": [_P, _I64, _I64, _I64, _I, _P, _I, _P, _P, _P, _P],
+    "svdq_chain_workspace_size": [_LP, _LP, _I64, C.POINTER(_SZ)],
+    "svdq_linear_forward_chain": [_LP, _LP, _P, _I64, _I64, _P, _I64, _P, _SZ, _P, _SZ, C.c_uint, _P],
     "svdq_int4_group_partials": [_LP, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P],
 }
 
@@ -306,6 +308,25 @@ class SVDQLinear:
         _call("svdq_gemm_forward", C.byref(self.layer), M, _t_ptr(Y), Y.stride(0), _t_ptr(ws), ws.numel(),
               FLAG_GELU if gelu else 0, _stream(stream))
         return Y
+
+    def forward_chain(self, nxt: "SVDQLinear", X, gelu: bool = False, Y=None, ws=None, ws_next=None,
+                      stream=None):
+        """Run this layer on X with nxt's activation pass in the GEMM
+        epilogue.  Returns ws_next (nxt's codes, scales and T); finish with
+        nxt.gemm(M, Y2, ws_next).  Y: optional output of this layer."""
+        import torch
+        assert X.dim() == 2 and X.shape[1] == self.K and X.stride(1) == 1
+        M = X.shape[0]
+        out = _SZ(0)
+        _call("svdq_chain_workspace_size", C.byref(self.layer), C.byref(nxt.layer), M, C.byref(out))
+        if ws is None:
+            ws = torch.empty(out.value, dtype=torch.uint8, device=X.device)
+        if ws_next is None:
+            ws_next = nxt.workspace(M)
+        _call("svdq_linear_forward_chain", C.byref(self.layer), C.byref(nxt.layer), _t_ptr(X), M, X.stride(0),
+              _t_ptr(Y), Y.stride(0) if Y is not None else 0, _t_ptr(ws), ws.numel(),
+              _t_ptr(ws_next), ws_next.numel(), FLAG_GELU if gelu else 0, _stream(stream))
+        return ws_next
 
     def workspace_export(self, M: int, ws=None, stream=None):
         ws = self._ws if ws is None else ws

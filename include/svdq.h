@@ -181,6 +181,31 @@ svdq_status svdq_quantize_activations(const svdq_layer* layer, const void* X_dev
 svdq_status svdq_gemm_forward(const svdq_layer* layer, int64_t M, void* Y_dev, int64_t ldy,
                               const void* ws_dev, size_t ws_bytes, unsigned flags, hipStream_t stream);
 
+/* Epilogue chaining of two layers where the output of `first` is the input
+ * of `next` (an MLP's fc1 -> fc2).  The pages' engine keeps operations that
+ * share an input in one kernel (SVDQuant §4.3, Fig. 6); here the same idea
+ * runs across a layer boundary: the 4-bit GEMM of `first` computes, in its
+ * epilogue and from the 16-bit output bits it would store, `next`'s
+ * smoothing, group quantization (codes and scales into ws_next_dev) and
+ * fp32 partial down-projections (one slab per 256 output columns of `first`,
+ * in ws_dev); a small kernel then sums the slabs in a fixed order and rounds
+ * T once into ws_next_dev.  The activation pass of `next` over `first`'s
+ * output is gone; svdq_gemm_forward(next, M, ..., ws_next_dev, ...) finishes
+ * `next`.  Codes and scales are identical to what svdq_quantize_activations
+ * writes for that output; T differs only in fp32 summation order.
+ * Requires: both layers MXFP4 (else SVDQ_ERR_UNSUPPORTED), the same dtype
+ * (else SVDQ_ERR_INVALID_ARG), first->N == next->K (else SVDQ_ERR_SHAPE).
+ * X_dev as for svdq_linear_forward on `first`; Y_dev may be NULL (the
+ * output of `first` is then not stored; else as for svdq_linear_forward);
+ * flags: SVDQ_FLAG_GELU for `first`.  ws_dev: >= svdq_chain_workspace_size
+ * bytes; ws_next_dev: >= svdq_workspace_size(next, M) bytes; both 256-byte
+ * aligned and not overlapping.  Deterministic.  Asynchronous. */
+svdq_status svdq_chain_workspace_size(const svdq_layer* first, const svdq_layer* next, int64_t M, size_t* bytes);
+svdq_status svdq_linear_forward_chain(const svdq_layer* first, const svdq_layer* next, const void* X_dev,
+                                      int64_t M, int64_t ldx, void* Y_dev, int64_t ldy, void* ws_dev,
+                                      size_t ws_bytes, void* ws_next_dev, size_t ws_next_bytes, unsigned flags,
+                                      hipStream_t stream);
+
 /* Calibration statistic for smoothing (SVDQuant §4.2): absmax_dev[k] =
  * max(absmax_dev[k], max_m |X[m,k]|), fp32, exact.  Initialise absmax_dev to
  * zero before the first batch.  Asynchronous. */

@@ -100,6 +100,11 @@ def test_lora_capacity_and_forward_arg_errors():
     assert rc == 1
     assert lib.svdq_workspace_size(C.byref(L), -1, C.byref(C.c_size_t())) == 1
     assert S.workspace_size(L, 1) >= 256 * 256 // 2
+    # chaining also needs device layers; nothing is launched
+    assert lib.svdq_chain_workspace_size(C.byref(L), C.byref(L), 16, C.byref(C.c_size_t())) == 1
+    rc = lib.svdq_linear_forward_chain(C.byref(L), C.byref(L), S._np_ptr(ws), 16, 256, None, 0, S._np_ptr(ws),
+                                       ws.size, S._np_ptr(ws), ws.size, 0, None)
+    assert rc == 1
 
 
 @pytest.mark.parametrize("dtype", [o.F16, o.BF16])
