@@ -161,12 +161,13 @@ struct K1Params {
 // Latency.  The vector memory counter retires in issue order, so waiting for
 // a short (L2) load also waits for every older HBM load.  A wave therefore
 // works in chunks of K1Chunk steps: it issues the X of the whole chunk at
-// once, quantizes the steps as they arrive (in order), and only then runs
-// the chunk's down-projection from the X still in registers, with the L1x
-// fragments -- the only loads in flight by then -- streamed two steps
-// ahead.  Every memory operation is unconditional (indices past the wave's
-// last step are clamped, so padding steps rewrite identical codes and add
-// zero to T), which keeps the compiler's counter bookkeeping exact.
+// once and takes the steps as they arrive (in order): quantize, then the
+// step's down-projection MFMAs from the X still in registers (they run on
+// the matrix unit under the next step's quantization), with the L1x
+// fragments streamed two steps ahead.  Every memory operation is
+// unconditional (indices past the wave's last step are clamped, so padding
+// steps rewrite identical codes; their MFMAs are skipped), which keeps the
+// compiler's counter bookkeeping exact.
 // invlambda is copied to LDS by direct global->LDS loads before anything
 // else, when it fits.
 constexpr int K1_IL_LDS_MAX_K = 16384;
@@ -184,19 +185,55 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   const int mt = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
-  const int64_t row = int64_t(mt) * 16 + m;
-  const bool valid = row < p.M;
+  // Rows past M (the workspace's padding up to its 256-row multiple) repeat
+  // row M - 1: their codes, scales and T only ever meet GEMM outputs that are
+  // not stored, and every load stays unconditional.
+  const int64_t row = min(int64_t(mt) * 16 + m, p.M - 1);
   const int nsteps = int(p.K / KSTEP);
   const int nmine = (nsteps - wave + 3) / 4;     // this wave's steps: wave, wave + 4, ...
-  const uint16_t* xrow = p.X + (valid ? row : 0) * p.ldx + 8 * q;
+  // MXFP4: lane group q holds the whole 32-block q of each step (k in
+  // [32q + 8c, +8) for load c); INT4: a quarter of every block (k in
+  // [32c + 8q, +8)), so a 64-group spans the four lanes of a token.
+  constexpr bool MXL = FMT == SVDQ_FMT_MXFP4_G32;
+  constexpr int XC = MXL ? 8 : 32;               // element stride between a lane's loads
+  const uint16_t* xrow = p.X + row * p.ldx + (MXL ? 32 : 8) * q;
   const float* il_lds = reinterpret_cast<const float*>(k1_lds);
   // invlambda is copied in whole 1 KB pieces, so its LDS copy spans K rounded up to 256
   f32x4* red = reinterpret_cast<f32x4*>(k1_lds + (IL_LDS ? size_t((p.K + 255) & ~int64_t(255)) * 4 : 0));   // [4][NJT][64]
 
+  // invlambda goes to LDS through registers and LDS stores, not direct
+  // global->LDS loads: after those the compiler makes the first LDS read
+  // wait for every outstanding load (all of the chunk's X).  Up to
+  // K = 4096 each thread holds its pieces while the chunk's X is requested
+  // and stores them afterwards; larger K copies first.
+  constexpr int ILR = 4;
+  const bool il_regs = p.K <= ILR * 1024;         // uniform
+  f32x4 ilv[ILR];
+  auto il_store = [&]() {
+#pragma unroll
+    for (int i = 0; i < ILR; ++i) {
+      const int pc = int(threadIdx.x) + 256 * i;
+      if (pc * 4 < p.K) *reinterpret_cast<f32x4*>(k1_lds + pc * 16) = ilv[i];
+    }
+    SVDQ_WAIT_LGKM0();
+    __builtin_amdgcn_s_barrier();
+  };
   if constexpr (IL_LDS) {
-    // wave w copies 1 KB pieces w, w + 4, ... of invlambda
-    for (int c = wave; c * 256 < p.K; c += 4)
-      lds_load16(p.invlam + c * 256 + lane * 4, k1_lds + c * 1024);
+    if (il_regs) {
+      // unconditional loads (an index past K/4 re-reads the last piece, which
+      // il_store does not store)
+      const int last = int(p.K / 4) - 1;
+#pragma unroll
+      for (int i = 0; i < ILR; ++i) {
+        const int pc = min(int(threadIdx.x) + 256 * i, last);
+        ilv[i] = *reinterpret_cast<const f32x4*>(p.invlam + pc * 4);
+      }
+    } else {
+      for (int pc = int(threadIdx.x); pc * 4 < p.K; pc += 256)
+        *reinterpret_cast<f32x4*>(k1_lds + pc * 16) = *reinterpret_cast<const f32x4*>(p.invlam + pc * 4);
+      SVDQ_WAIT_LGKM0();
+      __builtin_amdgcn_s_barrier();
+    }
   }
 
   f32x4 tacc[NJT > 0 ? NJT : 1];
@@ -211,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     const int s = step_of(i);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      xr[slot][c] = valid ? *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      xr[slot][c] = *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + XC * c);
   };
   auto load_l1x = [&](int slot, int i) {
     const int s = step_of(i);
@@ -228,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     float xh[4][8];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int k = s * KSTEP + 32 * c + 8 * q;
+      const int k = s * KSTEP + (MXL ? 32 * q + 8 * c : 32 * c + 8 * q);
       f32x4 il0, il1;
       if constexpr (IL_LDS) {
         il0 = *reinterpret_cast<const f32x4*>(il_lds + k);
@@ -262,19 +299,37 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
         const float sc = fminf(a / 7.0f, 65504.0f);
         sh[g] = f2h<SVDQ_F16>(sc);
         const float s32 = h2f<SVDQ_F16>(sh[g]);
+        // The code is rint(fl(x / s)).  x * fl(1/s) is within 1.5 ulp of
+        // fl(x / s), below 2^-19 wherever |x / s| < 10.5 (larger values
+        // clamp to 7 either way), so the two roundings can only differ when
+        // it lies within 2^-18 of a half-integer; such lanes redo the group
+        // with the correctly rounded division.
+        const float inv = s32 != 0.0f ? 1.0f / s32 : 0.0f;
+        bool near = false;
+        float r[2][8];
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float qv = xh[2 * g + cc][e] * inv;
+            r[cc][e] = rintf(qv);
+            near |= fabsf(qv - r[cc][e]) >= 0.5f - 0x1p-18f;
+          }
+        if (__builtin_expect(near, 0)) {
+#pragma unroll
+          for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[cc][e] = s32 != 0.0f ? rintf(xh[2 * g + cc][e] / s32) : 0.0f;
+        }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-          const int c = 2 * g + cc;
           unsigned v = 0u;
-          if (s32 != 0.0f) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              float r = rintf(xh[c][e] / s32);
-              r = fminf(fmaxf(r, -7.0f), 7.0f);
-              v |= (unsigned(int(r)) & 0xFu) << (4 * e);
-            }
+          for (int e = 0; e < 8; ++e) {
+            const float rc = fminf(fmaxf(r[cc][e], -7.0f), 7.0f);
+            v |= (unsigned(int(rc)) & 0xFu) << (4 * e);
           }
-          d[c] = v;
+          d[2 * g + cc] = v;
         }
       }
       uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
@@ -282,52 +337,38 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       if (q == 0)
         reinterpret_cast<unsigned*>(p.sx)[(size_t(mt) * nsteps + s) * 16 + m] = sh[0] | (sh[1] << 16);
     } else {
-      // block maxima across the four lanes of a token, all blocks at once
+      // the lane's own block: maximum, e8m0 exponent, 32 codes
+      float a = 0.0f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) am[c] = quad_max(am[c]);
-      int ex[4];
-      bool slow = false;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        ex[c] = e8m0_fast(am[c]);
-        slow |= e8m0_needs_slow(am[c]);
+      for (int c = 0; c < 4; ++c) a = fmaxf(a, am[c]);
+      int ex = e8m0_fast(a);
+      float scl = __uint_as_float(unsigned(ex) << 23);
+      if (__builtin_expect(e8m0_needs_slow(a), 0)) {
+        ex = e8m0_slow(a);
+        scl = ex != 0 ? __uint_as_float(unsigned(ex) << 23) : 1.0f;   // an all-zero block uses scale 1
       }
-      if (__builtin_expect(slow, 0)) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (e8m0_needs_slow(am[c])) ex[c] = e8m0_slow(am[c]);
-      }
+      // The packed fp32 -> E2M1 conversion divides by the power-of-two scale
+      // 2^(e-127) (exact) and rounds to the nearest E2M1 value, ties to the
+      // even mantissa, saturating at 6, keeping the sign of zero -- the group
+      // quantizer's rule.  Each call writes its two codes into the selected
+      // byte of the dword.
       unsigned d[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        // The packed fp32 -> E2M1 conversion divides by the power-of-two
-        // scale 2^(e-127) (exact) and rounds to the nearest E2M1 value, ties
-        // to the even mantissa, saturating at 6, keeping the sign of zero --
-        // the group quantizer's rule.  An all-zero block (e = 0) uses scale 1.
-        const int e = ex[c];
-        const float scl = e != 0 ? __uint_as_float(unsigned(e) << 23) : 1.0f;
         unsigned v = 0u;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const unsigned cv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xh[c][2 * b], xh[c][2 * b + 1], scl, 0);
-          v |= (cv & 0xFFu) << (8 * b);
-        }
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[c][0], xh[c][1], scl, 0);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[c][2], xh[c][3], scl, 1);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[c][4], xh[c][5], scl, 2);
+        v = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(v, xh[c][6], xh[c][7], scl, 3);
         d[c] = v;
       }
-      // 32-row fragment tile t32 = mt / 2; block c of the step -> half c / 2,
-      // lane (row in the 32-tile) + 32 (c % 2), bytes [4q, 4q + 4)
+      // 32-row fragment tile t32 = mt / 2; block q of the step -> half q / 2,
+      // lane (row in the 32-tile) + 32 (q % 2): one whole 16-byte piece
       const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint8_t* frag32 = p.xq + ((size_t(t32) * nsteps + s) * 2 + (c >> 1)) * 1024;
-        *reinterpret_cast<unsigned*>(frag32 + (r32 + 32 * (c & 1)) * 16 + 4 * q) = d[c];
-      }
-      // scale bytes 2 (t32 % 2) + h of the dword of lane (row + 32 (c % 2)):
-      // blocks (0, 2) and (1, 3) share a dword; lanes q = 0 and 1 write one each
-      if (q < 2) {
-        uint16_t* sxp = reinterpret_cast<uint16_t*>(p.sx + ((size_t(t32 >> 1) * nsteps + s) * 64 + r32 + 32 * q) * 4 + 2 * (t32 & 1));
-        *sxp = uint16_t(unsigned(ex[q]) | (unsigned(ex[q + 2]) << 8));
-      }
+      *reinterpret_cast<u32x4*>(p.xq + ((size_t(t32) * nsteps + s) * 2 + (q >> 1)) * 1024 + (r32 + 32 * (q & 1)) * 16) =
+          u32x4{d[0], d[1], d[2], d[3]};
+      // scale byte 2 (t32 % 2) + q / 2 of the dword of lane (row + 32 (q % 2))
+      p.sx[((size_t(t32 >> 1) * nsteps + s) * 64 + r32 + 32 * (q & 1)) * 4 + 2 * (t32 & 1) + (q >> 1)] = uint8_t(ex);
     }
   };
 
@@ -338,38 +379,29 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
 #pragma unroll
     for (int d = 0; d < CH; ++d) load_x(d, i0 + d);
     if constexpr (IL_LDS) {
-      if (i0 == 0) {
-        // the LDS copy of invlambda is complete once only the loads issued
-        // after it are outstanding; every wave's piece is visible after the barrier
-        SVDQ_WAIT_VM(LR * 4 * NJT + 4 * CH);
-        __builtin_amdgcn_s_barrier();
-      }
+      // the invlambda pieces arrived before this chunk's X (issued first)
+      if (i0 == 0 && il_regs) il_store();
     }
-#pragma unroll
-    for (int d = 0; d < CH; ++d)
-      if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
-    // down-projection T^T += L1x^T X^T on the raw 16-bit inputs (padding
-    // steps past the wave's last contribute zero)
+    // each step: quantize, then its share of the down-projection
+    // T^T += L1x^T X^T on the raw 16-bit inputs (the matrix unit runs it
+    // under the next step's quantization); a padding step past the wave's
+    // last (its index clamped, so it rewrites identical codes) adds nothing
 #pragma unroll
     for (int d = 0; d < CH; ++d) {
-      const bool real = i0 + d < nmine;
+      if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
+      if (i0 + d < nmine) {
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
+        for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u32x4 a = lring[d % LR][jt][c];
-          tacc[jt] = mfma16<DT>(real ? a : u32x4{0u, 0u, 0u, 0u}, xr[d][c], tacc[jt]);
-        }
+          for (int c = 0; c < 4; ++c) tacc[jt] = mfma16<DT>(lring[d % LR][jt][c], xr[d][c], tacc[jt]);
+      }
       if (d + LR < CH) load_l1x(d % LR, i0 + d + LR);
     }
   }
   if constexpr (IL_LDS) {
-    // a wave without K steps (K < 512) still meets the first chunk's barrier,
-    // so the T reduction's barrier pairs up across all four waves
-    if (nmine <= 0) {
-      SVDQ_WAIT_VM(0);
-      __builtin_amdgcn_s_barrier();
-    }
+    // a wave without K steps (K < 512) still stores its invlambda pieces and
+    // meets the first chunk's barrier, so the barriers pair up across waves
+    if (nmine <= 0 && il_regs) il_store();
   }
 
   if constexpr (NJT > 0) {
@@ -757,10 +789,11 @@ __device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t*
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
         if (x < nblk) {
-          const uint8_t* src = smem + (2 * wm + x) * (128 * mx::OUT_PITCH) + row * mx::OUT_PITCH + 16 * q;
+          // MFMA c takes k in [32q + 8c, +8) from lane group q (the MXFP4 L1x tiling)
+          const uint8_t* src = smem + (2 * wm + x) * (128 * mx::OUT_PITCH) + row * mx::OUT_PITCH + 64 * q;
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            acc = mfma16<DT>(la[x][c], *reinterpret_cast<const u32x4*>(src + 64 * c), acc);
+            acc = mfma16<DT>(la[x][c], *reinterpret_cast<const u32x4*>(src + 16 * c), acc);
         }
       }
       // lane holds T[token row][16 jt + 4 q + i]
@@ -1172,34 +1205,45 @@ __global__ __launch_bounds__(256) void k_up(UpParams p) {
 
 // -------------------------------------------------- INT4 per-group products
 // Finishes a chained down-projection: T[m][j] = round16(sum over the
-// column-tile slabs of the fp32 partials, in slab order), written in the
-// GEMM's low-rank operand layout.  One thread = one token x 8 consecutive
-// ranks (16 contiguous bytes in that layout).
+// column-tile slabs of the fp32 partials), written in the GEMM's low-rank
+// operand layout.  A workgroup covers 64 (token, 4-rank) items; its four
+// waves each sum a fixed quarter of the slabs and wave 0 adds the quarters
+// in order, so the result does not depend on scheduling.
 struct TfinParams {
   const float* tp;       // [nparts][Mp][slots]
   uint16_t* t;
   int64_t Mp;
-  int slots, nparts, ncols8;
+  int slots, nparts, ncols4;
 };
 
 template <int DT>
-__global__ __launch_bounds__(64) void k_tfin(TfinParams p) {
-  const int64_t g = int64_t(blockIdx.x) * 64 + threadIdx.x;
-  const int64_t m = g / p.ncols8;
-  const int j8 = int(g % p.ncols8);
-  if (m >= p.Mp) return;
-  const float* src = p.tp + m * p.slots + 8 * j8;
-  const size_t stride = size_t(p.Mp) * size_t(p.slots);
-  f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-  for (int q = 0; q < p.nparts; ++q) {
-    s0 += *reinterpret_cast<const f32x4*>(src + q * stride);
-    s1 += *reinterpret_cast<const f32x4*>(src + q * stride + 4);
+__global__ __launch_bounds__(256) void k_tfin(TfinParams p) {
+  __shared__ f32x4 part[3][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t g = int64_t(blockIdx.x) * 64 + lane;
+  const int64_t m = g / p.ncols4;
+  const int j4 = int(g % p.ncols4);
+  const bool ok = m < p.Mp;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (ok) {
+    const float* src = p.tp + m * p.slots + 4 * j4;
+    const size_t stride = size_t(p.Mp) * size_t(p.slots);
+    const int q0 = (p.nparts * w) / 4, q1 = (p.nparts * (w + 1)) / 4;
+#pragma unroll 4
+    for (int q = q0; q < q1; ++q) s += *reinterpret_cast<const f32x4*>(src + q * stride);
   }
-  // MXFP4 low-rank layout: 32-row tiles, 16-rank chunks, lane (row % 32) + 32 (j % 16 >= 8)
-  const int64_t t = m / 32, c = j8 / 2;
-  const int64_t ln = (m % 32) + 32 * (j8 % 2);
-  *reinterpret_cast<u32x4*>(p.t + ((t * (p.slots / 16) + c) * 64 + ln) * 8) =
-      u32x4{pack2<DT>(s0[0], s0[1]), pack2<DT>(s0[2], s0[3]), pack2<DT>(s1[0], s1[1]), pack2<DT>(s1[2], s1[3])};
+  if (w > 0) part[w - 1][lane] = s;
+  __syncthreads();
+  if (w == 0 && ok) {
+    s += part[0][lane];
+    s += part[1][lane];
+    s += part[2][lane];
+    // MXFP4 low-rank layout: 32-row tiles, 16-rank chunks, lane (row % 32) + 32 (j % 16 >= 8)
+    const int j = 4 * j4, c = j / 16, jj = j % 16;
+    const int64_t ln = (m % 32) + 32 * (jj / 8);
+    *reinterpret_cast<u32x2*>(p.t + (((m / 32) * (p.slots / 16) + c) * 64 + ln) * 8 + (jj % 8)) =
+        u32x2{pack2<DT>(s[0], s[1]), pack2<DT>(s[2], s[3])};
+  }
 }
 
 struct PartialParams {
@@ -1521,10 +1565,11 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
     tf.Mp = w.Mp;
     tf.slots = next->rank_slots;
     tf.nparts = mp.tiles_n;
-    tf.ncols8 = 2 * mp.nx_njt;
-    const int64_t n = w.Mp * tf.ncols8;
-    if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16>), dim3(unsigned((n + 63) / 64)), dim3(64), 0, stream, tf);
-    else hipLaunchKernelGGL((k_tfin<SVDQ_F16>), dim3(unsigned((n + 63) / 64)), dim3(64), 0, stream, tf);
+    tf.ncols4 = 4 * mp.nx_njt;
+    const int64_t n = w.Mp * tf.ncols4;
+    const dim3 grid(unsigned((n + 63) / 64));
+    if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16>), grid, dim3(256), 0, stream, tf);
+    else hipLaunchKernelGGL((k_tfin<SVDQ_F16>), grid, dim3(256), 0, stream, tf);
   }
   return launch_ok();
 }

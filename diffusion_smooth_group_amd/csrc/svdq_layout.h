@@ -27,7 +27,7 @@ constexpr int FRAG_BYTES = 1024;   // 64 lanes x 16 bytes
 constexpr int M_PAD = 256;         // workspace rows are padded to this
 constexpr int HDR_BYTES = 256;
 constexpr uint32_t BLOB_MAGIC = 0x51445653u;   // "SVDQ"
-constexpr uint32_t BLOB_VERSION = 1u;
+constexpr uint32_t BLOB_VERSION = 2u;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -149,13 +149,17 @@ inline size_t lr_pos(int64_t r, int64_t j, int slots, int fmt) {
 }
 
 // 16-bit L1x as the activation kernel reads it: (k, rank j).
-// Per (128-step, 16-rank tile, 32-K block c): 64 lanes x 8; lane covers
-// rank (j % 16) and k in [32c + 8q, 32c + 8q + 8) of the step, q = lane / 16
-// (the A operand of a 16 x 16 x 32 MFMA whose B operand is the same lane's
-// slice of X).
-inline size_t l1x_pos(int64_t k, int64_t j, int slots) {
-  int64_t s = k / KSTEP, kk = k % KSTEP, c = kk / 32, q = (kk % 32) / 8, e = kk % 8, jt = j / 16;
-  int64_t lane = (j % 16) + 16 * q;
+// Per (128-step, 16-rank tile, MFMA c = 0..3): 64 lanes x 8; lane covers
+// rank (j % 16) and 8 consecutive k of the step, the A operand of a
+// 16 x 16 x 32 MFMA whose B operand is the same lane's slice of X:
+//   INT4:  k in [32c + 8g, +8), g = lane / 16 (a lane holds a quarter of
+//          every 32-block of the step);
+//   MXFP4: k in [32g + 8c, +8) (lane group g holds the whole 32-block g).
+inline size_t l1x_pos(int64_t k, int64_t j, int slots, int fmt) {
+  const int64_t s = k / KSTEP, kk = k % KSTEP, e = kk % 8, jt = j / 16;
+  const int64_t c = fmt == 1 ? (kk % 32) / 8 : kk / 32;
+  const int64_t g = fmt == 1 ? kk / 32 : (kk % 32) / 8;
+  const int64_t lane = (j % 16) + 16 * g;
   return size_t((((s * (slots / 16) + jt) * 4 + c) * 64 + lane) * 8 + e);
 }
 

@@ -294,7 +294,7 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
   uint16_t* l1t = reinterpret_cast<uint16_t*>(blob + o.l1x);
   uint16_t* l2t = reinterpret_cast<uint16_t*>(blob + o.l2);
   for (int64_t j = 0; j < K; ++j)
-    for (int i = 0; i < rank; ++i) l1t[l1x_pos(j, i, slots)] = l1x[size_t(j) * rank + i];
+    for (int i = 0; i < rank; ++i) l1t[l1x_pos(j, i, slots, fmt)] = l1x[size_t(j) * rank + i];
   for (int i = 0; i < rank; ++i)
     for (int64_t n = 0; n < N; ++n) l2t[lr_pos(n, i, slots, fmt)] = l2q[size_t(i) * N + n];
   std::memcpy(blob + o.invlam, invlam.data(), size_t(K) * 4);
@@ -418,7 +418,7 @@ svdq_status write_lora(svdq_layer* L, const uint16_t* A, const uint16_t* B, int 
   for (int64_t k = 0; k < L->K; ++k)
     for (int j = L->rank; j < slots; ++j) {
       int i = j - L->rank;
-      l1t[l1x_pos(k, j, slots)] = (i < rL) ? A[size_t(k) * rL + i] : uint16_t(0);
+      l1t[l1x_pos(k, j, slots, L->fmt)] = (i < rL) ? A[size_t(k) * rL + i] : uint16_t(0);
     }
   for (int j = L->rank; j < slots; ++j) {
     int i = j - L->rank;
@@ -475,7 +475,7 @@ extern "C" svdq_status svdq_layer_export(const svdq_layer* L, float* lam, float*
   if (l1x) {
     uint16_t* o = static_cast<uint16_t*>(l1x);
     for (int64_t k = 0; k < K; ++k)
-      for (int j = 0; j < ra; ++j) o[size_t(k) * ra + j] = l1t[l1x_pos(k, j, slots)];
+      for (int j = 0; j < ra; ++j) o[size_t(k) * ra + j] = l1t[l1x_pos(k, j, slots, L->fmt)];
   }
   if (l2) {
     uint16_t* o = static_cast<uint16_t*>(l2);
