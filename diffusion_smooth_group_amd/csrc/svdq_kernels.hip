@@ -159,19 +159,20 @@ struct K1Params {
 // of lanes q = 0..3; an INT4 64-group is chunks 2g and 2g + 1 of those lanes.
 //
 // Latency.  The vector memory counter retires in issue order, so waiting for
-// a short (L2) load also waits for every older HBM load.  A wave therefore
-// works in chunks of K1Chunk steps: it issues the X of the whole chunk at
-// once and takes the steps as they arrive (in order): quantize, then the
-// step's down-projection MFMAs from the X still in registers (they run on
-// the matrix unit under the next step's quantization), with the L1x
-// fragments streamed two steps ahead.  Every memory operation is
-// unconditional (indices past the wave's last step are clamped, so padding
-// steps rewrite identical codes; their MFMAs are skipped), which keeps the
-// compiler's counter bookkeeping exact.
-// invlambda is copied to LDS by direct global->LDS loads before anything
-// else, when it fits.
+// a short (L2) load also waits for every older HBM load.  Each step is
+// quantized and then projected (the down-projection MFMAs from the X still
+// in registers run on the matrix unit under the next step's quantization).
+// MXFP4 requests a chunk of steps' X at once (the HBM stream runs at full
+// rate while the light quantizer catches up); INT4, with more VALU work per
+// byte, keeps a rolling ring of steps in flight so its quantization
+// overlaps the stream.  Every memory operation is unconditional (indices
+// past the wave's last step are clamped, so padding steps rewrite
+// identical codes; their MFMAs are skipped), which keeps the compiler's
+// counter bookkeeping exact.  invlambda is copied to LDS (when it fits)
+// through registers.
 constexpr int K1_IL_LDS_MAX_K = 16384;
-template <int NJT> struct K1Chunk { static constexpr int value = NJT <= 2 ? 6 : (NJT <= 4 ? 3 : 2); };
+template <int NJT> struct K1Ring { static constexpr int value = NJT <= 2 ? 3 : (NJT <= 4 ? 2 : 1); };
+template <int NJT> struct K1Chunk { static constexpr int value = NJT <= 2 ? 6 : 2; };
 template <int NJT> struct K1LRing { static constexpr int value = NJT <= 4 ? 2 : 1; };
 
 // QUANT = false runs the down-projection alone (the unfused low-rank
@@ -180,8 +181,12 @@ template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true>
 __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves per SIMD at least
   // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction buffer
   extern __shared__ __attribute__((aligned(16))) uint8_t k1_lds[];
-  constexpr int CH = K1Chunk<NJT>::value;
-  constexpr int LR = K1LRing<NJT>::value;
+  // MXFP4 (little VALU work per byte) requests a whole chunk of steps at
+  // once; INT4 (more VALU work per byte) and ranks above 64 (whose L1x
+  // fragments fill the registers) keep a rolling ring in flight
+  constexpr bool MXC = FMT == SVDQ_FMT_MXFP4_G32 && NJT <= 4;
+  constexpr int R = MXC ? K1Chunk<NJT>::value : K1Ring<NJT>::value;   // X slots
+  constexpr int LR = MXC ? K1LRing<NJT>::value : R;                    // L1x slots
   const int mt = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
@@ -241,8 +246,10 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   for (int j = 0; j < NJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int njc = p.njt > 0 ? p.njt - 1 : 0;
-  auto step_of = [&](int i) { return wave + 4 * (i < nmine ? i : nmine - 1); };
-  u32x4 xr[CH][4];
+  // the step of ring index i: clamped to the wave's last step, and step 0
+  // for a wave without steps (K < 512), whose ring prologue still loads
+  auto step_of = [&](int i) { return nmine > 0 ? wave + 4 * (i < nmine ? i : nmine - 1) : 0; };
+  u32x4 xr[R][4];
   u32x4 lring[LR][NJT > 0 ? NJT : 1][4];
   auto load_x = [&](int slot, int i) {
     const int s = step_of(i);
@@ -372,36 +379,68 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     }
   };
 
-  for (int i0 = 0; i0 < nmine; i0 += CH) {
-    // the chunk's first L1x fragments, then all of its X
+  // one step: quantize, then its share of the down-projection
+  // T^T += L1x^T X^T on the raw 16-bit inputs (the matrix unit runs it under
+  // the next step's quantization); a padding step past the wave's last (its
+  // index clamped, so it rewrites identical codes) adds nothing
+  auto project = [&](int slot, int lslot, int i) {
+    if (i < nmine) {
 #pragma unroll
-    for (int r = 0; r < LR; ++r) load_l1x(r, i0 + r);
+      for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-    for (int d = 0; d < CH; ++d) load_x(d, i0 + d);
-    if constexpr (IL_LDS) {
-      // the invlambda pieces arrived before this chunk's X (issued first)
-      if (i0 == 0 && il_regs) il_store();
+        for (int c = 0; c < 4; ++c) tacc[jt] = mfma16<DT>(lring[lslot][jt][c], xr[slot][c], tacc[jt]);
     }
-    // each step: quantize, then its share of the down-projection
-    // T^T += L1x^T X^T on the raw 16-bit inputs (the matrix unit runs it
-    // under the next step's quantization); a padding step past the wave's
-    // last (its index clamped, so it rewrites identical codes) adds nothing
+  };
+  if constexpr (MXC) {
+    // chunks of R steps: the L1x of the first LR steps, then all of the
+    // chunk's X; the steps are taken as they land, L1x streamed LR ahead
+    for (int i0 = 0; i0 < nmine; i0 += R) {
 #pragma unroll
-    for (int d = 0; d < CH; ++d) {
-      if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
-      if (i0 + d < nmine) {
+      for (int r = 0; r < LR; ++r) load_l1x(r, i0 + r);
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) tacc[jt] = mfma16<DT>(lring[d % LR][jt][c], xr[d][c], tacc[jt]);
+      for (int d = 0; d < R; ++d) load_x(d, i0 + d);
+      if constexpr (IL_LDS) {
+        // the invlambda pieces were requested before this chunk's X
+        if (i0 == 0 && il_regs) il_store();
       }
-      if (d + LR < CH) load_l1x(d % LR, i0 + d + LR);
+#pragma unroll
+      for (int d = 0; d < R; ++d) {
+        if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
+        project(d, d % LR, i0 + d);
+        if (d + LR < R) load_l1x(d % LR, i0 + d + LR);
+      }
     }
-  }
-  if constexpr (IL_LDS) {
-    // a wave without K steps (K < 512) still stores its invlambda pieces and
-    // meets the first chunk's barrier, so the barriers pair up across waves
-    if (nmine <= 0 && il_regs) il_store();
+    if constexpr (IL_LDS) {
+      // a wave without K steps (K < 512) still stores its invlambda pieces
+      // and meets the barrier, so the barriers pair up across waves
+      if (nmine <= 0 && il_regs) il_store();
+    }
+  } else {
+    // rolling ring of R steps: step i + R - 1 is requested (L1x first, then
+    // X) before step i is quantized and projected, so each wave keeps R
+    // steps in flight and its first steps return while later ones stream
+    // (with R = 1 the wide L1x of a large rank is requested after the
+    // quantization so it is not live across it)
+    auto load_step = [&](int slot, int i) {
+      if constexpr (R > 1) load_l1x(slot, i);
+      load_x(slot, i);
+    };
+#pragma unroll
+    for (int r = 0; r + 1 < R; ++r) load_step(r, r);
+    if constexpr (IL_LDS) {
+      // every wave stores its invlambda pieces (requested before any X) and
+      // meets this barrier, K steps or not
+      if (il_regs) il_store();
+    }
+    for (int i0 = 0; i0 < nmine; i0 += R) {
+#pragma unroll
+      for (int d = 0; d < R; ++d) {
+        load_step((d + R - 1) % R, i0 + d + R - 1);
+        if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
+        if constexpr (R == 1) load_l1x(d, i0 + d);
+        project(d, d, i0 + d);
+      }
+    }
   }
 
   if constexpr (NJT > 0) {
