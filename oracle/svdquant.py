@@ -26,6 +26,7 @@ import numpy as np
 
 INT4 = "int4_g64"
 MXFP4 = "mxfp4_g32"
+INT8 = "int8_w8a8"    # the 8-bit setting: per-token activations, per-channel weights
 F16 = "f16"
 BF16 = "bf16"
 GROUP = {INT4: 64, MXFP4: 32}
@@ -34,15 +35,16 @@ GROUP = {INT4: 64, MXFP4: 32}
 # 1 sign, 2 exponent, 1 mantissa bit; 0b000 = 0, 0b001 = 0.5 subnormal).
 E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)
 INT4_QMAX = 7      # signed b-bit integer: 2^(b-1) - 1 [SVDQuant §3]
+INT8_QMAX = 127    # the same rule for b = 8
 E2M1_QMAX = 6.0    # largest 4-bit float magnitude with 1 mantissa, 2 exponent bits [SVDQuant §3]
 FP16_MAX = 65504.0
 
 __all__ = [
-    "INT4", "MXFP4", "F16", "BF16", "GROUP", "E2M1_GRID",
+    "INT4", "MXFP4", "INT8", "F16", "BF16", "GROUP", "E2M1_GRID",
     "decode16", "round16", "round_sig",
     "activation_absmax", "weight_channel_absmax", "smoothing_factors",
     "smoothed_weight", "truncated_svd", "runtime_factors", "residual",
-    "quant_int4_g64", "quant_mxfp4_g32", "dequant_int4", "dequant_mxfp4",
+    "quant_int4_g64", "quant_mxfp4_g32", "dequant_int4", "dequant_mxfp4", "quant_int8_row", "dequant_int8",
     "quantize_groups", "dequantize_groups",
     "quantize_weight", "quantize_activations", "dequant_weight", "dequant_activations",
     "down_projection", "int4_group_partials", "main_product", "gelu_erf", "output_epilogue",
@@ -282,8 +284,37 @@ def dequant_mxfp4(codes: np.ndarray, e: np.ndarray) -> np.ndarray:
     return val * np.ldexp(1.0, np.asarray(e, dtype=np.int64) - 127)[..., None]
 
 
+def quant_int8_row(v: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """v: fp32 [..., L], one scale for the whole last axis (a token's row of
+    X_hat, or an output channel's column of R) [SVDQuant §5.1 implementation
+    details: the 8-bit setting quantizes activations per token, dynamically,
+    and weights per channel].  Returns (codes int8 in [-127, 127], fp32 scales
+    [..., 1]).
+
+    s = fl32(max|v| / 127) (reading: fp32 scale; the pages fix 16-bit scales
+    only for the INT4 groups); q = clamp(rint_half_even(fl32(v / s)),
+    -127, 127), q = 0 if s == 0.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    m = np.max(np.abs(v), axis=-1).astype(np.float32)
+    s = (m / np.float32(INT8_QMAX)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = (v / s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(ratio), -INT8_QMAX, INT8_QMAX)
+    q = np.where(s[..., None] == 0, 0.0, q)
+    q = np.nan_to_num(q, nan=0.0)
+    return q.astype(np.int8), s[..., None]
+
+
+def dequant_int8(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    return np.asarray(q, dtype=np.float64) * np.asarray(s, dtype=np.float64)
+
+
 def quantize_groups(v32: np.ndarray, fmt: str):
-    """Quantize the last axis of v32 in consecutive groups along it."""
+    """Quantize the last axis of v32 in consecutive groups along it (INT8:
+    one group spanning the whole axis)."""
+    if fmt == INT8:
+        return quant_int8_row(v32)
     G = GROUP[fmt]
     *lead, K = v32.shape
     assert K % G == 0, "K must be a multiple of the group size"
@@ -298,6 +329,8 @@ def quantize_groups(v32: np.ndarray, fmt: str):
 
 
 def dequantize_groups(q: np.ndarray, s: np.ndarray, fmt: str) -> np.ndarray:
+    if fmt == INT8:
+        return dequant_int8(q, s)
     G = GROUP[fmt]
     *lead, K = q.shape
     g = q.reshape(*lead, K // G, G)
@@ -307,8 +340,8 @@ def dequantize_groups(q: np.ndarray, s: np.ndarray, fmt: str) -> np.ndarray:
 
 def quantize_weight(R: np.ndarray, fmt: str) -> Tuple[np.ndarray, np.ndarray]:
     """Quantize the residual per output column n, groups along K.
-    Returns codes [K, N] (int8 INT4 values or uint8 E2M1 codes) and scales
-    [K/G, N] (fp16 bits or e8m0 bytes)."""
+    Returns codes [K, N] (int8 INT4 values, uint8 E2M1 codes, int8 INT8
+    values) and scales [K/G, N] (fp16 bits, e8m0 bytes; INT8: fp32 [1, N])."""
     q, s = quantize_groups(np.ascontiguousarray(np.asarray(R, dtype=np.float32).T), fmt)
     return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T)
 
@@ -361,7 +394,12 @@ def main_product(qx, sx, qw, sw, fmt: str) -> np.ndarray:
     INT4:  sum_g s_x[m,g] s_w[g,n] P_g[m,n]   (P_g exact integers)
     MXFP4: sum_b 2^(e_x + e_w - 254) sum_{k in b} e2m1(qx) e2m1(qw); both
            dequantized operands are exact in float64, so this is their product.
+    INT8:  s_x[m] s_w[n] P[m,n], P = sum_k qx[m,k] qw[k,n] exact (|P| <= K 127^2
+           < 2^53, so the float64 matrix product of the integer codes is exact).
     """
+    if fmt == INT8:
+        P = np.asarray(qx, dtype=np.float64) @ np.asarray(qw, dtype=np.float64)
+        return (np.asarray(sx, dtype=np.float64).reshape(-1, 1) * np.asarray(sw, dtype=np.float64).reshape(1, -1)) * P
     if fmt == INT4:
         P = int4_group_partials(qx, qw).astype(np.float64)
         sxf = np.asarray(sx, dtype=np.uint16).view(np.float16).astype(np.float64)   # [M, Gs]
