@@ -1,6 +1,6 @@
 """Benchmark of the SVDQuant linear (fused W4A4 + low-rank) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--fmt mxfp4|int4] [--workload fc1|...]
+    python bench.py [--steps K] [--warmup W] [--fmt mxfp4|int4|int8] [--workload fc1|...]
 
 A step is one forward of the layer -- activation kernel (smoothing, 4-bit
 group quantization, low-rank down-projection) then the 4-bit GEMM with the
@@ -30,7 +30,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective TOPS of fused W4A4+low-rank linear (FLUX fc1 shape), % of MFMA peak"
-PEAK_TFLOPS = {"mxfp4_g32": 10100.0, "int4_g64": 5000.0}     # MI355X dense MFMA: fp4, int8
+PEAK_TFLOPS = {"mxfp4_g32": 10100.0, "int4_g64": 5000.0, "int8_w8a8": 5000.0}   # MI355X dense MFMA: fp4, int8, int8
+FMT_NAMES = {"mxfp4": "mxfp4_g32", "int4": "int4_g64", "int8": "int8_w8a8"}
 HBM_PEAK_GBS = 8000.0
 
 WORKLOADS = {
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "int4"])
+    ap.add_argument("--fmt", default="mxfp4", choices=["mxfp4", "int4", "int8"],
+                    help="int8: the 8-bit setting (per-token / per-channel INT8; use --rank 16)")
     ap.add_argument("--workload", default="fc1", choices=sorted(WORKLOADS))
     ap.add_argument("--rank", type=int, default=32)
     ap.add_argument("--rotate", type=int, default=4, help="distinct X/Y/weight buffer sets cycled per step")
@@ -100,17 +102,21 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration": {"bytes_read": n, "bytes_written": n, "launches": 3}}), flush=True)
 
 
-def k1_bytes(M, K, r, fmt):
+def _codes_scales(rows, K, fmt):
+    """Bytes of one operand's codes and scales."""
+    if fmt == "int8_w8a8":
+        return rows * K + 4 * rows
     G = 64 if fmt == "int4_g64" else 32
     sb = 2 if fmt == "int4_g64" else 1
-    return 2 * M * K + M * K // 2 + (M * K // G) * sb + 2 * M * r + 2 * K * r + 4 * K
+    return rows * K // 2 + (rows * K // G) * sb
+
+
+def k1_bytes(M, K, r, fmt):
+    return 2 * M * K + _codes_scales(M, K, fmt) + 2 * M * r + 2 * K * r + 4 * K
 
 
 def k2_bytes(M, K, N, r, fmt):
-    G = 64 if fmt == "int4_g64" else 32
-    sb = 2 if fmt == "int4_g64" else 1
-    return (M * K // 2 + (M * K // G) * sb + K * N // 2 + (K * N // G) * sb + 2 * M * r + 2 * r * N
-            + 4 * N + 2 * M * N)
+    return _codes_scales(M, K, fmt) + _codes_scales(N, K, fmt) + 2 * M * r + 2 * r * N + 4 * N + 2 * M * N
 
 
 def cpu_baseline(spec, d, lin_export, fmt_name, rank):
@@ -152,8 +158,8 @@ def lowrank_study(args):
     import torch
     from diffusion_smooth_group_amd import svdq as S
     from diffusion_smooth_group_amd import workloads as wl
-    fmt_name = "mxfp4_g32" if args.fmt == "mxfp4" else "int4_g64"
-    fmt = S.FMT_MXFP4_G32 if args.fmt == "mxfp4" else S.FMT_INT4_G64
+    fmt_name = FMT_NAMES[args.fmt]
+    fmt = {"mxfp4": S.FMT_MXFP4_G32, "int4": S.FMT_INT4_G64, "int8": S.FMT_INT8_W8A8}[args.fmt]
     M, K, N, dts = WORKLOADS[args.workload]
     dt = S.BF16 if dts == "bf16" else S.F16
     spec = {"fc1": wl.config_shapes(3)[0], "fc2": wl.config_shapes(3)[1]}.get(args.workload, wl.config_shapes(2)[0])
@@ -333,8 +339,8 @@ def main():
     from diffusion_smooth_group_amd import svdq as S
     from diffusion_smooth_group_amd import workloads as wl
 
-    fmt_name = "mxfp4_g32" if args.fmt == "mxfp4" else "int4_g64"
-    fmt = S.FMT_MXFP4_G32 if args.fmt == "mxfp4" else S.FMT_INT4_G64
+    fmt_name = FMT_NAMES[args.fmt]
+    fmt = {"mxfp4": S.FMT_MXFP4_G32, "int4": S.FMT_INT4_G64, "int8": S.FMT_INT8_W8A8}[args.fmt]
     M, K, N, dts = WORKLOADS[args.workload]
     dt = S.BF16 if dts == "bf16" else S.F16
     if args.workload == "fc1":
@@ -439,7 +445,7 @@ def main():
     k1_gbs = k1_bytes(M, K, args.rank, fmt_name) / (k1_stats[0] * 1e-6) / 1e9
     peak = PEAK_TFLOPS[fmt_name]
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.fmt != "int8" else METRIC.replace("W4A4", "W8A8"),
         "value": round(tops, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -449,7 +455,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4" if fmt == S.FMT_MXFP4_G32 else "int4",
+        "dtype": args.fmt,
         "data": "synthetic",
         "config": {"workload": f"flux_{args.workload}_{M}x{K}x{N}", "M": M, "K": K, "N": N, "rank": args.rank,
                    "format": fmt_name, "activation_dtype": dts, "parallelism": "single GPU",

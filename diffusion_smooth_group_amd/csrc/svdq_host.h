@@ -93,6 +93,21 @@ inline void quant_int4_group(const float* v, int8_t* q, uint16_t* s_bits) {
   }
 }
 
+// INT8, one scale for a whole row of L values (an output channel of R):
+// s = fl32(max|v| / 127), q = clamp(rint(fl32(v / s)), -127, 127), 0 if s == 0.
+inline void quant_int8_row(const float* v, int64_t L, int8_t* q, float* s_out) {
+  float m = 0.0f;
+  for (int64_t i = 0; i < L; ++i) m = std::fmax(m, std::fabs(v[i]));
+  const float s = m / 127.0f;
+  *s_out = s;
+  for (int64_t i = 0; i < L; ++i) {
+    if (s == 0.0f) { q[i] = 0; continue; }
+    float r = std::nearbyint(v[i] / s);
+    r = std::fmin(std::fmax(r, -127.0f), 127.0f);
+    q[i] = std::isnan(r) ? 0 : int8_t(r);
+  }
+}
+
 // E2M1 magnitude index of a >= 0, nearest with ties to even, saturating at 6.
 inline uint32_t e2m1_index(float a) {
   return uint32_t(a > 0.25f) + uint32_t(a >= 0.75f) + uint32_t(a > 1.25f) + uint32_t(a >= 1.75f) +

@@ -643,6 +643,273 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 }
 
 
+// ------------------------------------------------------------------- k1_w8
+// INT8 activation kernel (the 8-bit setting: one scale per token over all
+// of K, so a token's maximum must be known before any of its codes).  One
+// workgroup = 16 tokens; its four waves take the 128-deep steps round robin
+// in the INT4 lane layout (lane m + 16q holds k in [32c + 8q, +8) of chunk
+// c), so L1x and T use the INT4 tilings.  Pass 1 streams X: the running max
+// of |x_hat| and the down-projection T on the 16 x 16 x 32 MFMA.  The token
+// maxima meet across the four lanes of a token and the four waves in LDS.
+// Pass 2 streams the workgroup's X again (96 KB at K = 3072, mostly from L2)
+// and writes the codes; each lane's 8 codes of a chunk are 8 contiguous
+// bytes of the INT8 fragment.  Both passes keep the next step's loads in
+// flight; rows past M repeat row M - 1.
+template <int DT, int NJT>
+__global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
+  __shared__ float smax[4][16];
+  __shared__ f32x4 red[4][NJT > 0 ? NJT : 1][64];
+  const int mt = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int m = lane & 15, q = lane >> 4;
+  const int64_t row = min(int64_t(mt) * 16 + m, p.M - 1);
+  const int nsteps = int(p.K / KSTEP);
+  const int nmine = (nsteps - wave + 3) / 4;
+  const uint16_t* xrow = p.X + row * p.ldx + 8 * q;
+  const int njc = p.njt > 0 ? p.njt - 1 : 0;
+  auto step_of = [&](int i) { return nmine > 0 ? wave + 4 * (i < nmine ? i : nmine - 1) : 0; };
+  auto load_x = [&](u32x4 (&x)[4], int i) {
+    const int s = step_of(i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + 32 * c);
+  };
+  auto load_l1x = [&](u32x4 (&l)[NJT > 0 ? NJT : 1][4], int i) {
+    const int s = step_of(i);
+    const u32x4* l1 = reinterpret_cast<const u32x4*>(p.l1x) + (size_t(s) * (p.slots / 16)) * 4 * 64 + lane;
+#pragma unroll
+    for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) l[jt][c] = l1[((jt < njc ? jt : njc) * 4 + c) * 64];
+  };
+  // x_hat = x * invlambda (one fp32 multiply), the same values in both passes
+  auto smooth = [&](const u32x4 (&x)[4], int s, float (&xh)[4][8]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int k = s * KSTEP + 32 * c + 8 * q;
+      const f32x4 il0 = *reinterpret_cast<const f32x4*>(p.invlam + k);
+      const f32x4 il1 = *reinterpret_cast<const f32x4*>(p.invlam + k + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x4& il = e < 2 ? il0 : il1;
+        xh[c][2 * e] = h2f<DT>(x[c][e] & 0xFFFFu) * il[(2 * e) & 3];
+        xh[c][2 * e + 1] = h2f<DT>(x[c][e] >> 16) * il[(2 * e + 1) & 3];
+      }
+    }
+  };
+  f32x4 tacc[NJT > 0 ? NJT : 1];
+#pragma unroll
+  for (int j = 0; j < NJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float am = 0.0f;
+  auto pass1_step = [&](const u32x4 (&x)[4], const u32x4 (&l)[NJT > 0 ? NJT : 1][4], int i) {
+    float xh[4][8];
+    smooth(x, step_of(i), xh);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xh[c][e]));
+    if (i < nmine) {
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) tacc[jt] = mfma16<DT>(l[jt][c], x[c], tacc[jt]);
+    }
+  };
+  if constexpr (NJT <= 4) {
+    u32x4 xa[4], xb[4];
+    u32x4 la[NJT > 0 ? NJT : 1][4], lb[NJT > 0 ? NJT : 1][4];
+    load_l1x(la, 0);
+    load_x(xa, 0);
+    for (int i = 0; i < nmine; i += 2) {
+      load_l1x(lb, i + 1);
+      load_x(xb, i + 1);
+      pass1_step(xa, la, i);
+      load_l1x(la, i + 2);
+      load_x(xa, i + 2);
+      pass1_step(xb, lb, i + 1);
+    }
+  } else {
+    // ranks above 64: the wide L1x is loaded once per step, after X
+    u32x4 xa[4];
+    u32x4 la[NJT][4];
+    for (int i = 0; i < nmine; ++i) {
+      load_x(xa, i);
+      load_l1x(la, i);
+      pass1_step(xa, la, i);
+    }
+  }
+  am = quad_max(am);
+  if (q == 0) smax[wave][m] = am;
+#pragma unroll
+  for (int jt = 0; jt < NJT; ++jt) red[wave][jt][lane] = tacc[jt];
+  __syncthreads();
+  const float tmax = fmaxf(fmaxf(smax[0][m], smax[1][m]), fmaxf(smax[2][m], smax[3][m]));
+  const float sc = tmax / 127.0f;
+  const float inv = sc != 0.0f ? 1.0f / sc : 0.0f;
+  if (wave == 0 && q == 0) reinterpret_cast<float*>(p.sx)[size_t(mt) * 16 + m] = sc;
+  if constexpr (NJT > 0) {
+    // T = the four waves' partial sums (fixed order), rounded once, in the
+    // INT4 low-rank layout (16-row tiles, 32-rank chunks)
+    for (int jt = wave; jt < p.njt; jt += 4) {
+      f32x4 v = red[0][jt][lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += red[w][jt][lane];
+      const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
+      uint16_t* dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+    }
+  }
+  // pass 2: codes rint(x_hat / s), from x_hat * (1/s) except for lanes whose
+  // quotient lies within 2^-15 of a half-integer (|x_hat / s| <= 127 keeps
+  // x_hat * fl(1/s) within 2^-16 of fl(x_hat / s)), which redo it with the
+  // correctly rounded division; clamp to +-127
+  auto pass2_step = [&](const u32x4 (&x)[4], int i) {
+    const int s = step_of(i);
+    float xh[4][8];
+    smooth(x, s, xh);
+    float r[4][8];
+    bool near = false;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = xh[c][e] * inv;
+        r[c][e] = rintf(qv);
+        near |= fabsf(qv - r[c][e]) >= 0.5f - 0x1p-15f;
+      }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[c][e] = sc != 0.0f ? rintf(xh[c][e] / sc) : 0.0f;
+    }
+    const int nst64 = int(p.K / 64);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      unsigned d[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float rc = fminf(fmaxf(r[c][e], -127.0f), 127.0f);
+        d[e >> 2] |= (unsigned(int(rc)) & 0xFFu) << (8 * (e & 3));
+      }
+      // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, lane group 2(c % 2) + q/2, byte 8(q % 2) + e
+      const size_t frag = (size_t(mt) * nst64 + 2 * s + (c >> 1)) * 64 + m + 16 * (2 * (c & 1) + (q >> 1));
+      *reinterpret_cast<u32x2*>(p.xq + frag * 16 + 8 * (q & 1)) = u32x2{d[0], d[1]};
+    }
+  };
+  {
+    u32x4 xa[4], xb[4];
+    load_x(xa, 0);
+    for (int i = 0; i < nmine; i += 2) {
+      load_x(xb, i + 1);
+      pass2_step(xa, i);
+      load_x(xa, i + 2);
+      pass2_step(xb, i + 1);
+    }
+  }
+}
+
+// ------------------------------------------------------------------- k2_w8
+// INT8 GEMM (the 8-bit setting).  One workgroup = 128 output columns x 128
+// tokens; 4 waves in a 2 x 2 grid, each 64 x 64 (4 x 4 tiles of 16 x 16 on
+// V_MFMA_I32_16X16X64_I8).  With one scale per token and per channel there
+// is nothing to dequantize inside the K loop: the int32 accumulators chain
+// through every MFMA (exact; |sum| <= K 127^2 < 2^31 for K < 133000) and the
+// epilogue applies s_x[m] s_w[n], then adds T L2 (a separate 16-bit MFMA
+// accumulator), the bias and GELU.  Operands for the next 128-deep step are
+// loaded while the current step's 32 MFMAs run.
+template <int DT, bool GELU>
+__global__ __launch_bounds__(256, 2) void k2_w8(K2Params p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int q = lane >> 4;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
+  const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
+  const int64_t nt0 = n0 / 16, mt0 = m0 / 16;
+  const int nsteps = int(p.K / KSTEP);
+  const int nst64 = int(p.K / 64);
+  const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq);
+  const u32x4* xq = reinterpret_cast<const u32x4*>(p.xq);
+  struct Ops {
+    u32x4 a[4][2], b[4][2];
+  };
+  auto load = [&](Ops& o, int s) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o.a[i][h] = wq[((nt0 + i) * nst64 + 2 * s + h) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o.b[j][h] = xq[((mt0 + j) * nst64 + 2 * s + h) * 64 + lane];
+    }
+  };
+  i32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
+  auto compute = [&](const Ops& o) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, o.a[i][h]),
+                                                            __builtin_bit_cast(i32x4, o.b[j][h]), acc[i][j], 0, 0, 0);
+  };
+  Ops o0, o1;
+  load(o0, 0);
+  int s = 0;
+  for (; s + 2 <= nsteps; s += 2) {
+    load(o1, s + 1);
+    compute(o0);
+    load(o0, s + 2 < nsteps ? s + 2 : nsteps - 1);
+    compute(o1);
+  }
+  if (s < nsteps) compute(o0);
+
+  // epilogue: s_x s_w P + T L2 + bias [-> GELU], rounded once
+  f32x4 lr[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lr[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4* l2 = reinterpret_cast<const u32x4*>(p.l2);
+  const u32x4* tt = reinterpret_cast<const u32x4*>(p.t);
+  for (int c = 0; c < p.nchunks; ++c) {
+    u32x4 la[4], tb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) la[i] = l2[((nt0 + i) * (p.slots / 32) + c) * 64 + lane];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tb[j] = tt[((mt0 + j) * (p.slots / 32) + c) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lr[i][j] = mfma16<DT>(la[i], tb[j], lr[i][j]);
+  }
+  const float* swf = reinterpret_cast<const float*>(p.sw);
+  const float* sxf = reinterpret_cast<const float*>(p.sx);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t n = n0 + 16 * i + 4 * q;
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n);
+    const f32x4 sw = *reinterpret_cast<const f32x4*>(swf + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t m = m0 + 16 * j + (lane & 15);
+      if (m < p.M) {
+        const float sx = sxf[m];
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = (float(acc[i][j][r]) * (sx * sw[r]) + lr[i][j][r]) + bv[r];
+          if constexpr (GELU) v[r] = gelu_erf(v[r]);
+        }
+        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------ k2_mx (MXFP4)
 // One workgroup = 256 output columns x 256 tokens, 4 waves in a 2 x 2 grid,
 // each 128 x 128 = 4 x 4 tiles of 32 x 32 on V_MFMA_SCALE_F32_32X32X64_F8F6F4
@@ -1362,6 +1629,22 @@ void launch_k1_proj(const K1Params& kp, int64_t Mp, hipStream_t st) {
 }
 
 template <int DT>
+void launch_k1_w8(const K1Params& kp, int64_t Mp, hipStream_t st) {
+  const dim3 grid(unsigned(Mp / 16)), block(256);
+  if (kp.njt == 0) hipLaunchKernelGGL((k1_w8<DT, 0>), grid, block, 0, st, kp);
+  else if (kp.njt <= 2) hipLaunchKernelGGL((k1_w8<DT, 2>), grid, block, 0, st, kp);
+  else if (kp.njt <= 4) hipLaunchKernelGGL((k1_w8<DT, 4>), grid, block, 0, st, kp);
+  else hipLaunchKernelGGL((k1_w8<DT, MAXJT>), grid, block, 0, st, kp);
+}
+
+template <int DT>
+void launch_k2_w8(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
+  dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
+  if (gelu) hipLaunchKernelGGL((k2_w8<DT, true>), grid, dim3(256), 0, st, kp);
+  else hipLaunchKernelGGL((k2_w8<DT, false>), grid, dim3(256), 0, st, kp);
+}
+
+template <int DT>
 void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
   if (gelu) hipLaunchKernelGGL((k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
@@ -1433,6 +1716,12 @@ void run_k1(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx, uint
            : L->fmt == SVDQ_FMT_MXFP4_G32 ? int(svdq::ceil_div(L->rank_active, 16))
                                          : 2 * int(svdq::ceil_div(L->rank_active, 32));
   kp.xq = ws + w.xq; kp.sx = ws + w.sx; kp.t = reinterpret_cast<uint16_t*>(ws + w.t);
+  if (L->fmt == SVDQ_FMT_INT8_W8A8) {
+    // one kernel for codes, scales and T (the separate-pass modes are not built for INT8)
+    if (L->dtype == SVDQ_BF16) launch_k1_w8<SVDQ_BF16>(kp, w.Mp, stream);
+    else launch_k1_w8<SVDQ_F16>(kp, w.Mp, stream);
+    return;
+  }
   if (mode == K1_PROJ) {
     if (kp.njt == 0) return;
     if (L->fmt == SVDQ_FMT_INT4_G64) {
@@ -1476,7 +1765,10 @@ K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, con
 void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
             bool gelu, bool lowrank, hipStream_t stream) {
   const K2Params kp = k2_params(L, M, Y_dev, ldy, ws, w, lowrank);
-  if (L->fmt == SVDQ_FMT_INT4_G64) {
+  if (L->fmt == SVDQ_FMT_INT8_W8A8) {
+    if (L->dtype == SVDQ_BF16) launch_k2_w8<SVDQ_BF16>(kp, w.Mp, gelu, stream);
+    else launch_k2_w8<SVDQ_F16>(kp, w.Mp, gelu, stream);
+  } else if (L->fmt == SVDQ_FMT_INT4_G64) {
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
     else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
   } else {
@@ -1650,6 +1942,7 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
   if (!mx_offsets_fit(L, w)) return SVDQ_ERR_UNSUPPORTED;
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
+  if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) != 0u && L->fmt == SVDQ_FMT_INT8_W8A8) return SVDQ_ERR_UNSUPPORTED;
   if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) == 0u || L->rank_active == 0) {
     run_k1(L, X_dev, M, ldx, ws, w, K1_BOTH, stream);
     run_k2(L, M, Y_dev, ldy, ws, w, gelu, true, stream);

@@ -16,6 +16,9 @@
 //          second.  (The order of k inside a group is free for an integer
 //          dot product; this one lets the activation kernel write each
 //          lane's 16 bytes straight from coalesced loads of X.)
+//   INT8 (16 x 16 x 64 integer MFMA): per 16-row tile and 64-deep K step,
+//          64 lanes x 16 bytes; lane l holds row l % 16 and the int8 codes of
+//          k in [16(l / 16), +16) of the step, one byte each.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -32,7 +35,11 @@ constexpr uint32_t BLOB_VERSION = 2u;
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
-inline int group_size(int fmt) { return fmt == 0 ? 64 : 32; }
+inline int group_size(int fmt) { return fmt == 0 ? 64 : 32; }   // 4-bit formats
+constexpr int FMT_INT8 = 2;                                       // whole-row scales
+inline size_t code_bytes(int64_t rows, int64_t K, int fmt) {
+  return fmt == FMT_INT8 ? size_t(rows) * size_t(K) : size_t(rows) * size_t(K) / 2;
+}
 
 // Header at the start of every blob (all later offsets are relative to the blob).
 struct BlobHeader {
@@ -49,6 +56,7 @@ struct BlobOffsets {
 
 // bytes of the weight scales
 inline size_t weight_scale_bytes(int64_t K, int64_t N, int fmt) {
+  if (fmt == FMT_INT8) return size_t(N) * 4;                                // INT8: fp32 per output channel
   if (fmt == 1) return size_t(N) * size_t(K / 32);                          // MX: one byte per 32-block
   return size_t(N / 16) * size_t(K / KSTEP) * 64;                           // INT4: 2 groups x 16 rows x fp16
 }
@@ -60,7 +68,7 @@ inline BlobOffsets blob_offsets(int64_t K, int64_t N, int slots, int fmt) {
   o.lam = p;    p = align256(p + size_t(K) * 4);
   o.l1x = p;    p = align256(p + size_t(K) * slots * 2);
   o.l2 = p;     p = align256(p + size_t(slots) * N * 2);
-  o.wq = p;     p = align256(p + size_t(K) * N / 2);
+  o.wq = p;     p = align256(p + code_bytes(N, K, fmt));
   o.sw = p;     p = align256(p + weight_scale_bytes(K, N, fmt));
   o.bias = p;   p = align256(p + size_t(N) * 4);
   o.total = p;
@@ -73,6 +81,7 @@ struct WsOffsets {
 };
 
 inline size_t act_scale_bytes(int64_t Mp, int64_t K, int fmt) {
+  if (fmt == FMT_INT8) return size_t(Mp) * 4;                               // fp32 per token
   if (fmt == 1) return size_t(Mp) * size_t(K / 32);
   return size_t(Mp / 16) * size_t(K / KSTEP) * 64;
 }
@@ -81,7 +90,7 @@ inline WsOffsets ws_offsets(int64_t M, int64_t K, int slots, int fmt) {
   WsOffsets w;
   w.Mp = round_up(M > 0 ? M : 1, M_PAD);
   size_t p = 0;
-  w.xq = p; p = align256(p + size_t(w.Mp) * K / 2);
+  w.xq = p; p = align256(p + code_bytes(w.Mp, K, fmt));
   w.sx = p; p = align256(p + act_scale_bytes(w.Mp, K, fmt));
   w.t = p;  p = align256(p + size_t(w.Mp) * slots * 2);
   w.total = p;
@@ -90,11 +99,16 @@ inline WsOffsets ws_offsets(int64_t M, int64_t K, int slots, int fmt) {
 
 // ---- element -> position maps (used by the host pack and the exporters) ----
 
-// 4-bit code of (row r, k) in a fragment array with K columns: byte offset
-// and nibble (0 = low) within it.
+// Code of (row r, k) in a fragment array with K columns: byte offset and
+// nibble (0 = low) within it (INT8: the whole byte, nib = 0).
 inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int* nib) {
   const int64_t nsteps = K / KSTEP, s = k / KSTEP, kk = k % KSTEP;
-  if (fmt == 1) {
+  if (fmt == FMT_INT8) {
+    const int64_t t = r / 16, s64 = k / 64, k64 = k % 64;
+    const int64_t lane = (r % 16) + 16 * (k64 / 16);
+    *byte = size_t(((t * (K / 64) + s64) * 64 + lane) * 16 + k64 % 16);
+    *nib = 0;
+  } else if (fmt == 1) {
     int64_t t = r / 32, b = kk / 32, c = kk % 32, h = b / 2;
     int64_t lane = (r % 32) + 32 * (b % 2);
     *byte = size_t(((t * nsteps + s) * 2 + h) * 1024 + lane * 16 + c / 2);

@@ -41,7 +41,7 @@ namespace {
 int slots_for(int capacity) { return int(round_up(std::max(capacity, 0), 32)); }
 
 svdq_status check_common(int64_t K, int64_t N, int rank_capacity, int fmt, int dtype) {
-  if (fmt != SVDQ_FMT_INT4_G64 && fmt != SVDQ_FMT_MXFP4_G32) return SVDQ_ERR_INVALID_ARG;
+  if (fmt != SVDQ_FMT_INT4_G64 && fmt != SVDQ_FMT_MXFP4_G32 && fmt != SVDQ_FMT_INT8_W8A8) return SVDQ_ERR_INVALID_ARG;
   if (dtype != SVDQ_F16 && dtype != SVDQ_BF16) return SVDQ_ERR_INVALID_ARG;
   if (K <= 0 || N <= 0) return SVDQ_ERR_SHAPE;
   if (K % KSTEP != 0 || N % 128 != 0) return SVDQ_ERR_SHAPE;
@@ -143,12 +143,14 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
   }
   // One candidate split: 16-bit factors, the fp32 residual's codes and
   // scales per output column (canonical [N][K] / [N][K/G]), and its error.
-  const int G = group_size(fmt);
+  const bool i8 = fmt == SVDQ_FMT_INT8_W8A8;
+  const int64_t G = i8 ? K : group_size(fmt);   // INT8: one scale per output channel
   const int rk = std::max(rank, 1);
   struct Cand {
     std::vector<uint16_t> l1x, l2q;   // K x rank, rank x N
-    std::vector<uint8_t> q;           // INT4: int8 value; MXFP4: E2M1 code
+    std::vector<uint8_t> q;           // INT4 / INT8: int8 value; MXFP4: E2M1 code
     std::vector<uint16_t> sc;         // INT4: fp16 bits; MXFP4: e8m0
+    std::vector<float> sf;            // INT8: fp32 channel scales
     double err = 0.0;
   };
   auto what = [&](int64_t j, int64_t n) { return double(lam[j]) * double(W[size_t(j) * N + n]); };
@@ -167,6 +169,7 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
     return l2d;
   };
   auto deq = [&](const Cand& c, int64_t n, int64_t k) -> double {
+    if (i8) return double(int8_t(c.q[size_t(n) * K + k])) * double(c.sf[size_t(n)]);
     const size_t gi = size_t(n) * (K / G) + size_t(k / G);
     if (fmt == SVDQ_FMT_INT4_G64)
       return double(int8_t(c.q[size_t(n) * K + k])) * double(f16_to_f32(c.sc[gi]));
@@ -204,14 +207,18 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
     });
     c.q.assign(size_t(N) * K, 0);
     c.sc.assign(size_t(N) * (K / G), 0);
+    if (i8) c.sf.assign(size_t(N), 0.0f);
     parallel_for(N, [&](int64_t nb, int64_t ne) {
-      std::vector<int8_t> qi(64);
+      std::vector<int8_t> qi(i8 ? size_t(K) : 64);
       std::vector<uint8_t> qm(32);
       for (int64_t n = nb; n < ne; ++n)
         for (int64_t g = 0; g < K / G; ++g) {
           const float* v = &Rt[size_t(n) * K + g * G];
           uint8_t* qo = &c.q[size_t(n) * K + g * G];
-          if (fmt == SVDQ_FMT_INT4_G64) {
+          if (i8) {
+            quant_int8_row(v, K, qi.data(), &c.sf[size_t(n)]);
+            for (int64_t i = 0; i < K; ++i) qo[i] = uint8_t(qi[i]);
+          } else if (fmt == SVDQ_FMT_INT4_G64) {
             uint16_t sbits;
             quant_int4_group(v, qi.data(), &sbits);
             c.sc[size_t(n) * (K / G) + g] = sbits;
@@ -279,12 +286,14 @@ svdq_status pack_host(const void* W_host, int64_t K, int64_t N, int64_t ldw, int
     for (int64_t n = tb * 16; n < te * 16; ++n)
       for (int64_t g = 0; g < K / G; ++g) {
         const uint16_t sv = best.sc[size_t(n) * (K / G) + g];
-        if (fmt == SVDQ_FMT_INT4_G64) std::memcpy(sw + 2 * int4_wscale_pos(n, g, K), &sv, 2);
+        if (i8) std::memcpy(sw + 4 * n, &best.sf[size_t(n)], 4);
+        else if (fmt == SVDQ_FMT_INT4_G64) std::memcpy(sw + 2 * int4_wscale_pos(n, g, K), &sv, 2);
         else sw[mx_scale_pos(n, g, K)] = uint8_t(sv);
-        for (int i = 0; i < G; ++i) {
+        for (int64_t i = 0; i < G; ++i) {
           size_t byte; int nib;
           code_pos(n, g * G + i, K, fmt, &byte, &nib);
-          wq[byte] |= uint8_t((best.q[size_t(n) * K + g * G + i] & 0xF) << (4 * nib));
+          const uint8_t c = best.q[size_t(n) * K + g * G + i];
+          wq[byte] |= i8 ? c : uint8_t((c & 0xF) << (4 * nib));
         }
       }
   });
@@ -490,13 +499,15 @@ extern "C" svdq_status svdq_layer_export(const svdq_layer* L, float* lam, float*
         for (int64_t n = 0; n < N; ++n) {
           size_t byte; int nib;
           code_pos(n, k, K, L->fmt, &byte, &nib);
-          uint8_t c = (wq[byte] >> (4 * nib)) & 0xF;
+          uint8_t c = L->fmt == SVDQ_FMT_INT8_W8A8 ? wq[byte] : uint8_t((wq[byte] >> (4 * nib)) & 0xF);
           if (L->fmt == SVDQ_FMT_INT4_G64) c = uint8_t(int8_t(uint8_t(c << 4)) >> 4);   // sign-extend
           o[size_t(k) * N + n] = c;
         }
     });
   }
-  if (scales) {
+  if (scales && L->fmt == SVDQ_FMT_INT8_W8A8) {
+    std::memcpy(scales, v + L->off_sw, size_t(N) * 4);      // fp32 [1][N]
+  } else if (scales) {
     const int G = group_size(L->fmt);
     for (int64_t g = 0; g < K / G; ++g)
       for (int64_t n = 0; n < N; ++n) {
@@ -538,13 +549,15 @@ extern "C" svdq_status svdq_workspace_export(const svdq_layer* L, const void* ws
         for (int64_t k = 0; k < K; ++k) {
           size_t byte; int nib;
           code_pos(m, k, K, L->fmt, &byte, &nib);
-          uint8_t c = (xq[byte] >> (4 * nib)) & 0xF;
+          uint8_t c = L->fmt == SVDQ_FMT_INT8_W8A8 ? xq[byte] : uint8_t((xq[byte] >> (4 * nib)) & 0xF);
           if (L->fmt == SVDQ_FMT_INT4_G64) c = uint8_t(int8_t(uint8_t(c << 4)) >> 4);
           o[size_t(m) * K + k] = c;
         }
     });
   }
-  if (scales) {
+  if (scales && L->fmt == SVDQ_FMT_INT8_W8A8) {
+    std::memcpy(scales, h.data() + w.sx, size_t(M) * 4);    // fp32 [M][1]
+  } else if (scales) {
     const int G = group_size(L->fmt);
     for (int64_t m = 0; m < M; ++m)
       for (int64_t g = 0; g < K / G; ++g) {

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsvdq.so")
 
 FMT_INT4_G64 = 0
 FMT_MXFP4_G32 = 1
+FMT_INT8_W8A8 = 2
 F16 = 0
 BF16 = 1
 FLAG_GELU = 1
@@ -171,13 +172,16 @@ def svd_factors(W_bits: np.ndarray, dtype: int, act_absmax: Optional[np.ndarray]
 
 def layer_export(L: svdq_layer, stream=None):
     K, N, ra = L.K, L.N, L.rank_active
-    G = 64 if L.fmt == FMT_INT4_G64 else 32
     lam = np.zeros(K, np.float32)
     invlam = np.zeros(K, np.float32)
     l1x = np.zeros((K, max(ra, 1)), np.uint16)
     l2 = np.zeros((max(ra, 1), N), np.uint16)
-    codes = np.zeros((K, N), np.int8 if L.fmt == FMT_INT4_G64 else np.uint8)
-    scales = np.zeros((K // G, N), np.uint16 if L.fmt == FMT_INT4_G64 else np.uint8)
+    codes = np.zeros((K, N), np.uint8 if L.fmt == FMT_MXFP4_G32 else np.int8)
+    if L.fmt == FMT_INT8_W8A8:
+        scales = np.zeros((1, N), np.float32)
+    else:
+        G = 64 if L.fmt == FMT_INT4_G64 else 32
+        scales = np.zeros((K // G, N), np.uint16 if L.fmt == FMT_INT4_G64 else np.uint8)
     bias = np.zeros(N, np.float32)
     _call("svdq_layer_export", C.byref(L), _np_ptr(lam), _np_ptr(invlam), _np_ptr(l1x), _np_ptr(l2),
           _np_ptr(codes), _np_ptr(scales), _np_ptr(bias), _stream(stream))
@@ -330,10 +334,13 @@ class SVDQLinear:
 
     def workspace_export(self, M: int, ws=None, stream=None):
         ws = self._ws if ws is None else ws
-        K, ra = self.layer.K, self.layer.rank_active
-        G = 64 if self.layer.fmt == FMT_INT4_G64 else 32
-        codes = np.zeros((M, K), np.int8 if self.layer.fmt == FMT_INT4_G64 else np.uint8)
-        scales = np.zeros((M, K // G), np.uint16 if self.layer.fmt == FMT_INT4_G64 else np.uint8)
+        K, ra, fmt = self.layer.K, self.layer.rank_active, self.layer.fmt
+        codes = np.zeros((M, K), np.uint8 if fmt == FMT_MXFP4_G32 else np.int8)
+        if fmt == FMT_INT8_W8A8:
+            scales = np.zeros((M, 1), np.float32)
+        else:
+            G = 64 if fmt == FMT_INT4_G64 else 32
+            scales = np.zeros((M, K // G), np.uint16 if fmt == FMT_INT4_G64 else np.uint8)
         t = np.zeros((M, max(ra, 1)), np.uint16)
         _call("svdq_workspace_export", C.byref(self.layer), _t_ptr(ws), ws.numel(), M, _np_ptr(codes),
               _np_ptr(scales), _np_ptr(t), _stream(stream))

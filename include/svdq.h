@@ -50,7 +50,10 @@ typedef enum {
 
 typedef enum {
   SVDQ_FMT_INT4_G64 = 0,     /* signed INT4 codes in [-7, 7], group 64 along K, fp16 scales */
-  SVDQ_FMT_MXFP4_G32 = 1     /* E2M1 codes, group 32 along K, e8m0 (power-of-two) scales */
+  SVDQ_FMT_MXFP4_G32 = 1,    /* E2M1 codes, group 32 along K, e8m0 (power-of-two) scales */
+  SVDQ_FMT_INT8_W8A8 = 2     /* the 8-bit setting (SVDQuant §5.1 implementation details): signed
+                                INT8 codes in [-127, 127], one fp32 scale per output channel of
+                                the residual and, computed on the fly, per token of X_hat */
 } svdq_format;
 
 typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
@@ -217,14 +220,15 @@ svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int6
 /* Canonical (untiled) copies of a packed layer, written to host buffers;
  * any output pointer may be NULL.  lam, invlam: [K] fp32.  l1x: K x
  * rank_active 16-bit.  l2: rank_active x N 16-bit.  codes: K x N bytes
- * (INT4: int8 value in [-7, 7]; MXFP4: E2M1 code 0..15).  scales: (K/G) x N
- * (INT4: fp16 bits as uint16; MXFP4: e8m0 bytes).  bias: [N] fp32.
+ * (INT4: int8 value in [-7, 7]; MXFP4: E2M1 code 0..15; INT8: int8 value
+ * in [-127, 127]).  scales: (K/G) x N (INT4: fp16 bits as uint16; MXFP4:
+ * e8m0 bytes; INT8: 1 x N fp32).  bias: [N] fp32.
  * Synchronous (copies the blob from the device when it lives there). */
 svdq_status svdq_layer_export(const svdq_layer* layer, float* lam, float* invlam, void* l1x, void* l2,
                               void* codes, void* scales, float* bias, hipStream_t stream);
 
 /* Canonical copies of what svdq_quantize_activations wrote for M tokens:
- * codes M x K bytes (as above), scales M x (K/G), t: M x rank_active
+ * codes M x K bytes (as above), scales M x (K/G) (INT8: M x 1 fp32), t: M x rank_active
  * 16-bit (the rounded down-projection).  Synchronous. */
 svdq_status svdq_workspace_export(const svdq_layer* layer, const void* ws_dev, size_t ws_bytes, int64_t M,
                                   void* codes, void* scales, void* t, hipStream_t stream);

@@ -9,7 +9,7 @@ import oracle as o
 from diffusion_smooth_group_amd import svdq as S
 from diffusion_smooth_group_amd import workloads as wl
 
-FMTS = {o.INT4: S.FMT_INT4_G64, o.MXFP4: S.FMT_MXFP4_G32}
+FMTS = {o.INT4: S.FMT_INT4_G64, o.MXFP4: S.FMT_MXFP4_G32, o.INT8: S.FMT_INT8_W8A8}
 DTS = {o.F16: S.F16, o.BF16: S.BF16}
 
 # Output gate (floating point): relative Frobenius error <= 5e-3 and

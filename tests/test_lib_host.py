@@ -19,7 +19,7 @@ from diffusion_smooth_group_amd import workloads as wl
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HDR = os.path.join(ROOT, "include", "svdq.h")
-FMTS = {o.INT4: S.FMT_INT4_G64, o.MXFP4: S.FMT_MXFP4_G32}
+FMTS = {o.INT4: S.FMT_INT4_G64, o.MXFP4: S.FMT_MXFP4_G32, o.INT8: S.FMT_INT8_W8A8}
 DTS = {o.F16: S.F16, o.BF16: S.BF16}
 
 
@@ -108,7 +108,7 @@ def test_lora_capacity_and_forward_arg_errors():
 
 
 @pytest.mark.parametrize("dtype", [o.F16, o.BF16])
-@pytest.mark.parametrize("fmt", [o.INT4, o.MXFP4])
+@pytest.mark.parametrize("fmt", [o.INT4, o.MXFP4, o.INT8])
 @pytest.mark.parametrize("KN", [(256, 384), (640, 256)])
 def test_host_pack_bit_exact_given_factors(dtype, fmt, KN):
     K, N = KN
@@ -129,7 +129,8 @@ def test_host_pack_bit_exact_given_factors(dtype, fmt, KN):
     # residual codes and scales, recomputed by the oracle from the library's factors
     pf = o.pack_from_factors(d["W"], dtype, ex["lam"], ex["L1x"], ex["L2q"], fmt)
     assert np.array_equal(ex["codes"].astype(np.int64), pf["qw"].astype(np.int64))
-    assert np.array_equal(ex["scales"], pf["sw"])
+    assert ex["scales"].shape == pf["sw"].shape
+    assert np.array_equal(np.ascontiguousarray(ex["scales"]).view(np.uint8), np.ascontiguousarray(pf["sw"]).view(np.uint8))
     assert np.array_equal(ex["bias"], o.decode16(d["bias"], dtype).astype(np.float32))
 
 
