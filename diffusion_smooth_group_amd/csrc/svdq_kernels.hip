@@ -648,12 +648,12 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 // of K, so a token's maximum must be known before any of its codes).  One
 // workgroup = 16 tokens; its four waves take the 128-deep steps round robin
 // in the INT4 lane layout (lane m + 16q holds k in [32c + 8q, +8) of chunk
-// c), so L1x and T use the INT4 tilings.  Pass 1 streams X: the running max
+// c), so L1x uses the INT4 tiling.  Pass 1 streams X: the running max
 // of |x_hat| and the down-projection T on the 16 x 16 x 32 MFMA.  The token
 // maxima meet across the four lanes of a token and the four waves in LDS.
 // Pass 2 streams the workgroup's X again (96 KB at K = 3072, mostly from L2)
 // and writes the codes; each lane's 8 codes of a chunk are 8 contiguous
-// bytes of the INT8 fragment.  Both passes keep the next step's loads in
+// bytes of the INT8 fragment the GEMM (k2_mx with I8) reads.  Both passes keep the next step's loads in
 // flight; rows past M repeat row M - 1.
 template <int DT, int NJT>
 __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
@@ -748,13 +748,14 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   if (wave == 0 && q == 0) reinterpret_cast<float*>(p.sx)[size_t(mt) * 16 + m] = sc;
   if constexpr (NJT > 0) {
     // T = the four waves' partial sums (fixed order), rounded once, in the
-    // INT4 low-rank layout (16-row tiles, 32-rank chunks)
+    // GEMM's low-rank layout (32-row tiles, 16-rank chunks); lane holds
+    // T[m][16 jt + 4q + i]
     for (int jt = wave; jt < p.njt; jt += 4) {
       f32x4 v = red[0][jt][lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) v += red[w][jt][lane];
-      const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
-      uint16_t* dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
+      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+      uint16_t* dst = p.t + ((size_t(t32) * (p.slots / 16) + jt) * 64 + r32 + 32 * (q >> 1)) * 8 + 4 * (q & 1);
       *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
     }
   }
@@ -791,8 +792,10 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
         const float rc = fminf(fmaxf(r[c][e], -127.0f), 127.0f);
         d[e >> 2] |= (unsigned(int(rc)) & 0xFFu) << (8 * (e & 3));
       }
-      // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, lane group 2(c % 2) + q/2, byte 8(q % 2) + e
-      const size_t frag = (size_t(mt) * nst64 + 2 * s + (c >> 1)) * 64 + m + 16 * (2 * (c & 1) + (q >> 1));
+      // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, half c % 2, lane
+      // (row in the 32-row tile) + 32 (q / 2), byte 8 (q % 2) + e
+      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
+      const size_t frag = ((size_t(t32) * nst64 + 2 * s + (c >> 1)) * 2 + (c & 1)) * 64 + r32 + 32 * (q >> 1);
       *reinterpret_cast<u32x2*>(p.xq + frag * 16 + 8 * (q & 1)) = u32x2{d[0], d[1]};
     }
   };
@@ -804,108 +807,6 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
       pass2_step(xa, i);
       load_x(xa, i + 2);
       pass2_step(xb, i + 1);
-    }
-  }
-}
-
-// ------------------------------------------------------------------- k2_w8
-// INT8 GEMM (the 8-bit setting).  One workgroup = 128 output columns x 128
-// tokens; 4 waves in a 2 x 2 grid, each 64 x 64 (4 x 4 tiles of 16 x 16 on
-// V_MFMA_I32_16X16X64_I8).  With one scale per token and per channel there
-// is nothing to dequantize inside the K loop: the int32 accumulators chain
-// through every MFMA (exact; |sum| <= K 127^2 < 2^31 for K < 133000) and the
-// epilogue applies s_x[m] s_w[n], then adds T L2 (a separate 16-bit MFMA
-// accumulator), the bias and GELU.  Operands for the next 128-deep step are
-// loaded while the current step's 32 MFMAs run.
-template <int DT, bool GELU>
-__global__ __launch_bounds__(256, 2) void k2_w8(K2Params p) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int q = lane >> 4;
-  const int wn = wave & 1, wm = wave >> 1;
-  const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
-  const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
-  const int64_t nt0 = n0 / 16, mt0 = m0 / 16;
-  const int nsteps = int(p.K / KSTEP);
-  const int nst64 = int(p.K / 64);
-  const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq);
-  const u32x4* xq = reinterpret_cast<const u32x4*>(p.xq);
-  struct Ops {
-    u32x4 a[4][2], b[4][2];
-  };
-  auto load = [&](Ops& o, int s) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o.a[i][h] = wq[((nt0 + i) * nst64 + 2 * s + h) * 64 + lane];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o.b[j][h] = xq[((mt0 + j) * nst64 + 2 * s + h) * 64 + lane];
-    }
-  };
-  i32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = i32x4{0, 0, 0, 0};
-  auto compute = [&](const Ops& o) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, o.a[i][h]),
-                                                            __builtin_bit_cast(i32x4, o.b[j][h]), acc[i][j], 0, 0, 0);
-  };
-  Ops o0, o1;
-  load(o0, 0);
-  int s = 0;
-  for (; s + 2 <= nsteps; s += 2) {
-    load(o1, s + 1);
-    compute(o0);
-    load(o0, s + 2 < nsteps ? s + 2 : nsteps - 1);
-    compute(o1);
-  }
-  if (s < nsteps) compute(o0);
-
-  // epilogue: s_x s_w P + T L2 + bias [-> GELU], rounded once
-  f32x4 lr[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) lr[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4* l2 = reinterpret_cast<const u32x4*>(p.l2);
-  const u32x4* tt = reinterpret_cast<const u32x4*>(p.t);
-  for (int c = 0; c < p.nchunks; ++c) {
-    u32x4 la[4], tb[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) la[i] = l2[((nt0 + i) * (p.slots / 32) + c) * 64 + lane];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) tb[j] = tt[((mt0 + j) * (p.slots / 32) + c) * 64 + lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lr[i][j] = mfma16<DT>(la[i], tb[j], lr[i][j]);
-  }
-  const float* swf = reinterpret_cast<const float*>(p.sw);
-  const float* sxf = reinterpret_cast<const float*>(p.sx);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t n = n0 + 16 * i + 4 * q;
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n);
-    const f32x4 sw = *reinterpret_cast<const f32x4*>(swf + n);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + 16 * j + (lane & 15);
-      if (m < p.M) {
-        const float sx = sxf[m];
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = (float(acc[i][j][r]) * (sx * sw[r]) + lr[i][j][r]) + bv[r];
-          if constexpr (GELU) v[r] = gelu_erf(v[r]);
-        }
-        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
-      }
     }
   }
 }
@@ -977,6 +878,7 @@ struct MxParams {
 };
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 
@@ -1106,7 +1008,7 @@ __device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t*
   }
 }
 
-template <int DT, bool GELU, bool CHAIN = false>
+template <int DT, bool GELU, bool CHAIN = false, bool I8 = false>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   // one LDS object (a second one makes the compiler wait for every global->LDS
   // load before any LDS read)
@@ -1114,7 +1016,11 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   // the wave index is uniform: keep it (and every LDS address derived from it) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
-  const int nsteps = int(p.K / KSTEP);
+  // I8: the 8-bit setting on the same pipeline -- a step is 64 deep (2 KB
+  // of int8 codes per 32-row tile, like an MXFP4 128-deep step), the
+  // 32 x 32 x 32 int8 MFMA chains int32 accumulators, no scale loads
+  constexpr int LPS = I8 ? 8 : 10;         // global->LDS loads per wave and step
+  const int nsteps = int(p.K / (I8 ? 64 : KSTEP));
   const int64_t ntiles_n = p.N / 32;       // valid 32-row weight tiles
   const int cs = p.slots / 16;              // 16-rank chunks per tile in L2 / T
 
@@ -1181,6 +1087,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     }
     // one of the 10 loads a wave issues per K step
     auto issue_unit = [&](int r, uint8_t* base, int x) {
+      if (I8 && x >= 8) return;
       if (x < 4) dma16(rsb, ga[x] + r * 2048, base + mx::A_OFF + (4 * wave + x) * 1024);
       else if (x < 8) dma16(rsw, gb[x - 4] + r * 2048, base + mx::B_OFF + (4 * wave + x - 4) * 1024);
       else if (x == 8) dma4(rsb, osa + r * 256, base + mx::SA_OFF + wave * 256);
@@ -1197,14 +1104,16 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         dma16(rsb, int(tA[f] * cs + c) * 1024, base + mx::A_OFF + (4 * wave + f) * 1024);
         dma16(rsw, p.off_t + int(tB[f] * cs + c) * 1024, base + mx::B_OFF + (4 * wave + f) * 1024);
       }
-      dma4(rsb, osa, base + mx::SA_OFF + wave * 256);
-      dma4(rsw, osb, base + mx::SB_OFF + wave * 256);
+      if constexpr (!I8) {
+        dma4(rsb, osa, base + mx::SA_OFF + wave * 256);
+        dma4(rsw, osb, base + mx::SB_OFF + wave * 256);
+      }
     };
     auto issue = [&](int r, int st) {
       uint8_t* base = smem + st * mx::STAGE_BYTES;
       if (r < nk) {
 #pragma unroll
-        for (int x = 0; x < 10; ++x) issue_unit(r, base, x);
+        for (int x = 0; x < LPS; ++x) issue_unit(r, base, x);
       } else {
         issue_lr(r - nk, base);
       }
@@ -1221,15 +1130,23 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           F.a[i][h] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + ((4 * wn + i) * 2 + h) * 1024 + lane * 16);
-      F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
-      F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
-      F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
-      F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+      if constexpr (!I8) {
+        F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
+        F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
+        F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
+        F.sa1 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn + 1) * 256 + lane * 4);
+      }
     };
     // One MFMA of a K step (k = 0..31 walks h, i, j; the two halves of a
     // tile's K are 16 MFMAs apart, so no MFMA waits on its predecessor).
     auto mfma_k = [&](const Frags& F, int k) {
       const int h = k >> 4, i = (k >> 2) & 3, j = k & 3;
+      if constexpr (I8) {
+        acc[i][j] = __builtin_bit_cast(f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+            __builtin_bit_cast(i32x4, F.a[i][h]), __builtin_bit_cast(i32x4, F.b[j][h]),
+            __builtin_bit_cast(i32x16, acc[i][j]), 0, 0, 0));
+        return;
+      }
       const i32x8 a = i32x8{int(F.a[i][h][0]), int(F.a[i][h][1]), int(F.a[i][h][2]), int(F.a[i][h][3]), 0, 0, 0, 0};
       const i32x8 b = i32x8{int(F.b[j][h][0]), int(F.b[j][h][1]), int(F.b[j][h][2]), int(F.b[j][h][3]), 0, 0, 0, 0};
       acc[i][j] = mfma_mx32(a, b, acc[i][j], i < 2 ? F.sa0 : F.sa1, j < 2 ? F.sb0 : F.sb1, 2 * (i & 1) + h, 2 * (j & 1) + h);
@@ -1266,6 +1183,8 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       } else if (e < 16) {
         const int ee = e - 8;
         nxt.a[ee >> 1][ee & 1] = *reinterpret_cast<const u32x4*>(rb + mx::A_OFF + ((4 * wn + (ee >> 1)) * 2 + (ee & 1)) * 1024 + lane * 16);
+      } else if (I8) {
+        return;
       } else if (e == 16) {
         nxt.sb0 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
         nxt.sb1 = *reinterpret_cast<const int*>(rb + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
@@ -1282,7 +1201,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       // cur's LDS reads were issued an iteration ago; retire them here so the
       // 20 reads below need no counter slot (lgkmcnt counts at most 15)
       SVDQ_WAIT_LGKM0();
-      SVDQ_WAIT_VM(10);
+      SVDQ_WAIT_VM(LPS);
       __builtin_amdgcn_s_barrier();
       const uint8_t* rb = smem + ((r + 1) & 3) * mx::STAGE_BYTES;
       uint8_t* lb = smem + ((r + 3) & 3) * mx::STAGE_BYTES;
@@ -1298,11 +1217,17 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     auto body_tail = [&](int r, Frags& cur, Frags& nxt) {
       SVDQ_WAIT_LGKM0();
       if (r + 1 < nk) {
-        if (r + 2 < total) SVDQ_WAIT_VM(10);
+        if (r + 2 < total) SVDQ_WAIT_VM(LPS);
         else SVDQ_WAIT_VM(0);
         __builtin_amdgcn_s_barrier();
         if (r + 3 < total) issue(r + 3, (r + 3) & 3);
         read_frags(nxt, (r + 1) & 3);
+      } else if (r + 3 < total) {
+        // the last K step still requests step r + 3 (the third low-rank
+        // step, when there are more than four 16-rank chunks): its stage
+        // held step r - 1, which every wave read before the previous
+        // step's barrier
+        issue(r + 3, (r + 3) & 3);
       }
       compute(cur);
     };
@@ -1321,16 +1246,17 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
 #pragma unroll
     for (int r = 0; r < mx::STAGES - 1; ++r)
       if (r < total) issue(r, r);
-    if (total > 2) SVDQ_WAIT_VM(20);
-    else if (total > 1) SVDQ_WAIT_VM(10);
+    if (total > 2) SVDQ_WAIT_VM(2 * LPS);
+    else if (total > 1) SVDQ_WAIT_VM(LPS);
     else SVDQ_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     // Accumulators start at the bias: one 32 x 32 x 16 MFMA per tile with a
     // zero C operand (no separate zero fill or bias add).  A holds the
     // bias in k = 0..3 of lanes 0..31 (a 16-bit bias times 1.0 is exact), B of
     // tile column j holds 1.0 at k = j only, so each product picks the bias
-    // once and the 16 MFMAs stay distinct.
-    {
+    // once and the 16 MFMAs stay distinct.  (I8 starts from zero integers
+    // and adds the bias the same way once its sums are scaled to fp32.)
+    auto bias_mfma = [&](bool onto) {
       const bool lo = lane < 32;
       const unsigned one = lo ? (DT == SVDQ_BF16 ? 0x3F80u : 0x3C00u) : 0u;
 #pragma unroll
@@ -1340,9 +1266,17 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const u32x4 bj = u32x4{j == 0 ? one : j == 1 ? one << 16 : 0u, j == 2 ? one : j == 3 ? one << 16 : 0u, 0u, 0u};
-          acc[i][j] = mfma32x16<DT>(ab, bj, f32x16{});
+          acc[i][j] = mfma32x16<DT>(ab, bj, onto ? acc[i][j] : f32x16{});
         }
       }
+    };
+    if constexpr (I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    } else {
+      bias_mfma(false);
     }
     Frags F0, F1;
     read_frags(F0, 0);
@@ -1354,6 +1288,33 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     for (; r < nk; r += 2) {
       body_tail(r, F0, F1);
       if (r + 1 < nk) body_tail(r + 1, F1, F0);
+    }
+    if constexpr (I8) {
+      // the exact int32 sums -> fp32 times s_x[m] s_w[n] (accumulator 4gg + x
+      // of tile (i, j): column 32i + 8gg + 4(lane / 32) + x, token
+      // 32j + lane % 32), then the bias; the low-rank steps add onto them
+      const float* sxf = reinterpret_cast<const float*>(p.sx);
+      const float* swf = reinterpret_cast<const float*>(p.sw);
+      float sxv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sxv[j] = sxf[m0 + 128 * wm + 32 * j + (lane & 31)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x16 swv;                              // s_w of this lane's 16 columns of tile i
+#pragma unroll
+        for (int gg = 0; gg < 4; ++gg) {
+          int64_t nn = n0 + 128 * wn + 32 * i + 8 * gg + 4 * (lane >> 5);
+          nn = nn + 4 <= p.N ? nn : p.N - 4;    // columns of a partial last tile are never stored
+          const f32x4 sw = *reinterpret_cast<const f32x4*>(swf + nn);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) swv[4 * gg + x] = sw[x];
+        }
+        // whole-vector conversion (the int32 sums are a bit-cast view of the accumulators)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_convertvector(__builtin_bit_cast(i32x16, acc[i][j]), f32x16) * (swv * sxv[j]);
+      }
+      bias_mfma(true);
     }
     // low-rank steps (their loads were issued during the last K steps)
     for (int q = nk; q < total; ++q) {
@@ -1638,13 +1599,6 @@ void launch_k1_w8(const K1Params& kp, int64_t Mp, hipStream_t st) {
 }
 
 template <int DT>
-void launch_k2_w8(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
-  dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
-  if (gelu) hipLaunchKernelGGL((k2_w8<DT, true>), grid, dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL((k2_w8<DT, false>), grid, dim3(256), 0, st, kp);
-}
-
-template <int DT>
 void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
   if (gelu) hipLaunchKernelGGL((k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
@@ -1665,12 +1619,12 @@ MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   return mp;
 }
 
-template <int DT>
+template <int DT, bool I8 = false>
 void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   const MxParams mp = mx_params(kp, w);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
-  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true>), dim3(T), dim3(256), 0, st, mp);
-  else hipLaunchKernelGGL((k2_mx<DT, false>), dim3(T), dim3(256), 0, st, mp);
+  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
+  else hipLaunchKernelGGL((k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
 }
 
 template <int DT>
@@ -1766,8 +1720,8 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
             bool gelu, bool lowrank, hipStream_t stream) {
   const K2Params kp = k2_params(L, M, Y_dev, ldy, ws, w, lowrank);
   if (L->fmt == SVDQ_FMT_INT8_W8A8) {
-    if (L->dtype == SVDQ_BF16) launch_k2_w8<SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2_w8<SVDQ_F16>(kp, w.Mp, gelu, stream);
+    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16, true>(kp, w, gelu, stream);
+    else launch_k2_mx<SVDQ_F16, true>(kp, w, gelu, stream);
   } else if (L->fmt == SVDQ_FMT_INT4_G64) {
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
     else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
@@ -1780,7 +1734,7 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
 // the MXFP4 GEMM addresses the blob from L2 and the workspace from the
 // activation codes with 31-bit offsets
 bool mx_offsets_fit(const svdq_layer* L, const svdq::WsOffsets& w) {
-  if (L->fmt != SVDQ_FMT_MXFP4_G32) return true;
+  if (L->fmt == SVDQ_FMT_INT4_G64) return true;
   const size_t lim = size_t(1) << 31;
   return L->off_bias + size_t(L->N) * 4 - L->off_l2 < lim && w.total - w.xq < lim;
 }

@@ -16,9 +16,10 @@
 //          second.  (The order of k inside a group is free for an integer
 //          dot product; this one lets the activation kernel write each
 //          lane's 16 bytes straight from coalesced loads of X.)
-//   INT8 (16 x 16 x 64 integer MFMA): per 16-row tile and 64-deep K step,
-//          64 lanes x 16 bytes; lane l holds row l % 16 and the int8 codes of
-//          k in [16(l / 16), +16) of the step, one byte each.
+//   INT8 (32 x 32 x 32 integer MFMA): per 32-row tile and 64-deep K step,
+//          2 halves x 64 lanes x 16 bytes; in half h, lane l holds row l % 32
+//          and the int8 codes of k in [32h + 16(l / 32), +16) of the step --
+//          the same 2 KB per tile and step as an MXFP4 128-deep step.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -104,9 +105,9 @@ inline WsOffsets ws_offsets(int64_t M, int64_t K, int slots, int fmt) {
 inline void code_pos(int64_t r, int64_t k, int64_t K, int fmt, size_t* byte, int* nib) {
   const int64_t nsteps = K / KSTEP, s = k / KSTEP, kk = k % KSTEP;
   if (fmt == FMT_INT8) {
-    const int64_t t = r / 16, s64 = k / 64, k64 = k % 64;
-    const int64_t lane = (r % 16) + 16 * (k64 / 16);
-    *byte = size_t(((t * (K / 64) + s64) * 64 + lane) * 16 + k64 % 16);
+    const int64_t t = r / 32, s64 = k / 64, h = (k % 64) / 32, k32 = k % 32;
+    const int64_t lane = (r % 32) + 32 * (k32 / 16);
+    *byte = size_t((((t * (K / 64) + s64) * 2 + h) * 64 + lane) * 16 + k32 % 16);
     *nib = 0;
   } else if (fmt == 1) {
     int64_t t = r / 32, b = kk / 32, c = kk % 32, h = b / 2;
@@ -147,12 +148,12 @@ inline size_t int4_xscale_pos(int64_t m, int64_t G, int64_t K) {
 
 // 16-bit low-rank operand of the GEMM epilogue: (row r, rank j), rows are
 // n for L2 and m for T.
-//   MXFP4 (32 x 32 x 16 MFMA): per (32-row tile, 16-rank chunk) 64 lanes x 8;
+//   MXFP4 and INT8 (32 x 32 x 16 MFMA): per (32-row tile, 16-rank chunk) 64 lanes x 8;
 //          lane l holds row l % 32 and j in [16c + 8(l / 32), +8).
 //   INT4 (16 x 16 x 32 MFMA): per (16-row tile, 32-rank chunk) 64 lanes x 8;
 //          lane l holds row l % 16 and j in [32c + 8(l / 16), +8).
 inline size_t lr_pos(int64_t r, int64_t j, int slots, int fmt) {
-  if (fmt == 1) {
+  if (fmt == 1 || fmt == FMT_INT8) {
     int64_t t = r / 32, c = j / 16, jj = j % 16;
     int64_t lane = (r % 32) + 32 * (jj / 8);
     return size_t(((t * (slots / 16) + c) * 64 + lane) * 8 + jj % 8);

@@ -72,6 +72,15 @@ def test_unfused_lowrank_qkv_sampled():
 
 
 @pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
+@pytest.mark.parametrize("K", [256, 1024])
+def test_branch_wider_than_64(fmt, K):
+    # rank 64 + LoRA 32: six 16-rank chunks, three low-rank pipeline steps
+    # in the MXFP4 GEMM (the third one is requested by the last K step)
+    d = _small(96, K, 256, o.BF16, fmt, 64, lora=32, seed=70 + K)
+    G.run_layer_case(d, fmt, 64, lora=True)
+
+
+@pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
 def test_refined_pack_forward(fmt):
     # a pack whose low-rank split was refined (device blob written through
     # svdq_pack_weights_ex) meets the same gates
