@@ -681,19 +681,17 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) l[jt][c] = l1[((jt < njc ? jt : njc) * 4 + c) * 64];
   };
-  // x_hat = x * invlambda (one fp32 multiply), the same values in both passes
-  auto smooth = [&](const u32x4 (&x)[4], int s, float (&xh)[4][8]) {
+  // x_hat = x * invlambda (one fp32 multiply) for chunk c of step s, the
+  // same values in both passes
+  auto smooth_c = [&](const u32x4& xc, int s, int c, float (&xh)[8]) {
+    const int k = s * KSTEP + 32 * c + 8 * q;
+    const f32x4 il0 = *reinterpret_cast<const f32x4*>(p.invlam + k);
+    const f32x4 il1 = *reinterpret_cast<const f32x4*>(p.invlam + k + 4);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int k = s * KSTEP + 32 * c + 8 * q;
-      const f32x4 il0 = *reinterpret_cast<const f32x4*>(p.invlam + k);
-      const f32x4 il1 = *reinterpret_cast<const f32x4*>(p.invlam + k + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f32x4& il = e < 2 ? il0 : il1;
-        xh[c][2 * e] = h2f<DT>(x[c][e] & 0xFFFFu) * il[(2 * e) & 3];
-        xh[c][2 * e + 1] = h2f<DT>(x[c][e] >> 16) * il[(2 * e + 1) & 3];
-      }
+    for (int e = 0; e < 4; ++e) {
+      const f32x4& il = e < 2 ? il0 : il1;
+      xh[2 * e] = h2f<DT>(xc[e] & 0xFFFFu) * il[(2 * e) & 3];
+      xh[2 * e + 1] = h2f<DT>(xc[e] >> 16) * il[(2 * e + 1) & 3];
     }
   };
   f32x4 tacc[NJT > 0 ? NJT : 1];
@@ -701,12 +699,13 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   for (int j = 0; j < NJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float am = 0.0f;
   auto pass1_step = [&](const u32x4 (&x)[4], const u32x4 (&l)[NJT > 0 ? NJT : 1][4], int i) {
-    float xh[4][8];
-    smooth(x, step_of(i), xh);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < 4; ++c) {
+      float xh[8];
+      smooth_c(x[c], step_of(i), c, xh);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xh[c][e]));
+      for (int e = 0; e < 8; ++e) am = fmaxf(am, fabsf(xh[e]));
+    }
     if (i < nmine) {
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
@@ -765,36 +764,31 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   // correctly rounded division; clamp to +-127
   auto pass2_step = [&](const u32x4 (&x)[4], int i) {
     const int s = step_of(i);
-    float xh[4][8];
-    smooth(x, s, xh);
-    float r[4][8];
-    bool near = false;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float qv = xh[c][e] * inv;
-        r[c][e] = rintf(qv);
-        near |= fabsf(qv - r[c][e]) >= 0.5f - 0x1p-15f;
-      }
-    if (__builtin_expect(near, 0)) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[c][e] = sc != 0.0f ? rintf(xh[c][e] / sc) : 0.0f;
-    }
     const int nst64 = int(p.K / 64);
+    const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
+      float xh[8], r[8];
+      smooth_c(x[c], s, c, xh);
+      bool near = false;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = xh[e] * inv;
+        r[e] = rintf(qv);
+        near |= fabsf(qv - r[e]) >= 0.5f - 0x1p-15f;
+      }
+      if (__builtin_expect(near, 0)) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = sc != 0.0f ? rintf(xh[e] / sc) : 0.0f;
+      }
       unsigned d[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float rc = fminf(fmaxf(r[c][e], -127.0f), 127.0f);
+        const float rc = fminf(fmaxf(r[e], -127.0f), 127.0f);
         d[e >> 2] |= (unsigned(int(rc)) & 0xFFu) << (8 * (e & 3));
       }
       // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, half c % 2, lane
       // (row in the 32-row tile) + 32 (q / 2), byte 8 (q % 2) + e
-      const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
       const size_t frag = ((size_t(t32) * nst64 + 2 * s + (c >> 1)) * 2 + (c & 1)) * 64 + r32 + 32 * (q >> 1);
       *reinterpret_cast<u32x2*>(p.xq + frag * 16 + 8 * (q & 1)) = u32x2{d[0], d[1]};
     }
