@@ -982,23 +982,29 @@ __device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t*
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         la[x][c] = x < nblk ? l1x[((size_t(n0 / KSTEP + x) * cs + jt) * 4 + c) * 64 + lane] : u32x4{0u, 0u, 0u, 0u};
+    // the four 16-token blocks accumulate side by side (four independent
+    // MFMA chains instead of one)
+    f32x4 acc[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int row = 64 * wn + 16 * u + (lane & 15);
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        if (x < nblk) {
-          // MFMA c takes k in [32q + 8c, +8) from lane group q (the MXFP4 L1x tiling)
-          const uint8_t* src = smem + (2 * wm + x) * (128 * mx::OUT_PITCH) + row * mx::OUT_PITCH + 64 * q;
+    for (int x = 0; x < 2; ++x) {
+      if (x < nblk) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc = mfma16<DT>(la[x][c], *reinterpret_cast<const u32x4*>(src + 16 * c), acc);
-        }
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            // MFMA c takes k in [32q + 8c, +8) from lane group q (the MXFP4 L1x tiling)
+            const int row = 64 * wn + 16 * u + (lane & 15);
+            const uint8_t* src = smem + (2 * wm + x) * (128 * mx::OUT_PITCH) + row * mx::OUT_PITCH + 64 * q + 16 * c;
+            acc[u] = mfma16<DT>(la[x][c], *reinterpret_cast<const u32x4*>(src), acc[u]);
+          }
       }
-      // lane holds T[token row][16 jt + 4 q + i]
-      *reinterpret_cast<f32x4*>(tp + size_t(16 * u + (lane & 15)) * p.nx_slots + 16 * jt + 4 * q) = acc;
     }
+    // lane holds T[token row][16 jt + 4 q + i]
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<f32x4*>(tp + size_t(16 * u + (lane & 15)) * p.nx_slots + 16 * jt + 4 * q) = acc[u];
   }
 }
 
