@@ -42,6 +42,14 @@ def test_mxfp4_many_tiles_full_parity():
     G.run_layer_case(d, o.MXFP4, 16, lora=True, gelu=True)
 
 
+def test_mxfp4_more_tiles_than_cus_full_parity():
+    # 17 x 16 = 272 tiles of 256 x 256: more than the 256 compute units, so
+    # the persistent GEMM walks several tiles per workgroup; ragged tokens
+    # (4300 of a 4352-row workspace), GELU, LoRA, every output checked
+    d = _small(4300, 256, 4096, o.BF16, o.MXFP4, 16, lora=16, seed=33)
+    G.run_layer_case(d, o.MXFP4, 16, lora=True, gelu=True)
+
+
 @pytest.mark.parametrize("K", [128, 256, 384])
 @pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
 def test_short_k_wide_low_rank(fmt, K):
