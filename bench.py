@@ -120,7 +120,8 @@ def k2_bytes(M, K, N, r, fmt):
 
 
 def cpu_baseline(spec, d, lin_export, fmt_name, rank):
-    """The oracle's float32 forward on a bounded sample of the layer."""
+    """The oracle's forward (float64, as the parity tests use it) on a bounded
+    sample of the layer."""
     import threadpoolctl  # noqa: F401  (reports the BLAS threads)
     from threadpoolctl import threadpool_info
     import oracle as o
@@ -132,10 +133,10 @@ def cpu_baseline(spec, d, lin_export, fmt_name, rank):
              "L1x": lin_export["L1x"], "L2q": L2q, "qw": pf["qw"], "sw": pf["sw"],
              "bias": None if d["bias"] is None else d["bias"][:cols]}
     Xs = np.ascontiguousarray(d["X"][:rows])
-    o.forward_fp32_timed(layer, Xs)          # warm (dequantizes the weight once)
+    o.forward(layer, Xs)                     # warm
     reps, t0 = 0, time.perf_counter()
     while True:
-        o.forward_fp32_timed(layer, Xs)
+        o.forward(layer, Xs)
         reps += 1
         el = time.perf_counter() - t0
         if el > 8.0 or reps >= 20:
@@ -144,9 +145,9 @@ def cpu_baseline(spec, d, lin_export, fmt_name, rank):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": 2.0 * rows * spec.K * cols / t / 1e12, "unit": "TOPS", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{rows} of {spec.M} tokens x {cols} of {spec.N} output columns, oracle float32 path "
-                      f"(activation quantization, dequantized sgemm, up-projection, bias), {reps} reps, "
-                      f"{t * 1e3:.1f} ms each; host os.cpu_count()={os.cpu_count()}"}
+            "sample": f"{rows} of {spec.M} tokens x {cols} of {spec.N} output columns, the oracle's float64 "
+                      f"forward (activation quantization, exact 4-bit product, down- and up-projection, bias, "
+                      f"one rounding), {reps} reps, {t * 1e3:.1f} ms each; host os.cpu_count()={os.cpu_count()}"}
 
 
 def lowrank_study(args):

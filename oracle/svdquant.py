@@ -49,7 +49,7 @@ __all__ = [
     "quantize_weight", "quantize_activations", "dequant_weight", "dequant_activations",
     "down_projection", "int4_group_partials", "main_product", "gelu_erf", "output_epilogue",
     "output_epilogue_f64",
-    "pack", "pack_from_factors", "attach_lora", "forward", "forward_fp32_timed",
+    "pack", "pack_from_factors", "attach_lora", "forward",
     "quantization_error", "prop41_bound", "lowrank_overhead", "packed_bytes",
     "split_error", "refine_split",
 ]
@@ -541,25 +541,6 @@ def forward(layer: Dict[str, object], X_bits, gelu: bool = False, return_parts: 
     Y = round16(Y64, dt)
     if return_parts:
         return Y, {"qx": qx, "sx": sx, "xhat": xh, "T": T, "Ymain": Ym, "Y64": Y64}
-    return Y
-
-
-def forward_fp32_timed(layer: Dict[str, object], X_bits, gelu: bool = False):
-    """The same forward with float32 dequantized products (the CPU-baseline
-    variant: vectorized quantization, one BLAS sgemm on dequantized operands,
-    the up-projection and the bias).  Not bit-faithful; used for timing."""
-    dt, fmt = layer["dtype"], layer["fmt"]
-    X = decode16(X_bits, dt).astype(np.float32)
-    qx, sx, _ = quantize_activations(X, layer["invlam"], fmt)
-    xd = dequant_activations(qx, sx, fmt).astype(np.float32)
-    if "_wd32" not in layer:
-        layer["_wd32"] = dequant_weight(layer["qw"], layer["sw"], fmt).astype(np.float32)
-    T = (X @ decode16(layer["L1x"], dt).astype(np.float32))
-    Y = xd @ layer["_wd32"] + T @ decode16(layer["L2q"], dt).astype(np.float32)
-    if layer.get("bias") is not None:
-        Y += decode16(layer["bias"], dt).astype(np.float32)[None, :]
-    if gelu:
-        Y = gelu_erf(Y).astype(np.float32)
     return Y
 
 
