@@ -483,6 +483,7 @@ struct K2Params {
   uint16_t* Y;
   int64_t ldy, M, N, K;
   int slots, nchunks, nchunks16;
+  float zero;   // 0.0f, passed at run time (the INT4 scale products use it)
 };
 
 __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
@@ -515,14 +516,30 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return x < 0.0f ? h : x - h;
 }
 
+// Exact product of two fp16 scales, each the low or high half of a word, as
+// one v_fma_mix_f32 (the f16 operands are widened inside the instruction).
+// z is a runtime zero: with a literal 0 the compiler drops the addend and
+// emits two conversions and a multiply instead.  The product of two fp16
+// values is exact in fp32, so this equals float(a) * float(b).
+__device__ __forceinline__ float hprod(unsigned a, int ha, unsigned b, int hb, float z) {
+  const _Float16 x = __builtin_bit_cast(_Float16, (unsigned short)(ha ? a >> 16 : a & 0xFFFFu));
+  const _Float16 y = __builtin_bit_cast(_Float16, (unsigned short)(hb ? b >> 16 : b & 0xFFFFu));
+  return __builtin_fmaf((float)x, (float)y, z);
+}
+
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
 // 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per 64-group the
 // integer MFMA gives the exact partial P_g (the nibbles are widened to
 // 16 q per byte, so the MFMA sums 256 P_g); it is dequantized on the VALU
-// into fp32 accumulators: acc += f32(P) * (s_w * s_x / 256).  That dequant
-// bounds the kernel, so the accumulators live in VGPRs, each step's operands
-// and scales are loaded one step ahead, and two waves share a SIMD (one's
-// MFMAs run under the other's VALU work).
+// into fp32 accumulators: acc += f32(256 P) * (s_w * s_x), and the epilogue
+// takes the factor 2^-8 back out (exact: scaling by a power of two commutes
+// with every rounding on the way).  Per accumulator and group that is three
+// VALU instructions (scale product, conversion, fused multiply-add), which
+// bound the kernel; so the accumulators live in VGPRs, operands and scales
+// are buffer loads with the lane's offset fixed and the step's offset in
+// scalar registers (no per-step address arithmetic on the VALU), each step
+// loaded one step ahead, and two waves share a SIMD (one's MFMAs run under
+// the other's VALU work).
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -530,13 +547,18 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
   const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
-  const int64_t nt0 = n0 / 16, mt0 = m0 / 16;
+  const int nt0 = int(n0 / 16), mt0 = int(m0 / 16);
   const int nsteps = int(p.K / KSTEP);
+  const float z = p.zero;
 
-  const u32x4* wq = reinterpret_cast<const u32x4*>(p.wq);
-  const u32x4* xq = reinterpret_cast<const u32x4*>(p.xq);
-  const uint16_t* sw16 = reinterpret_cast<const uint16_t*>(p.sw);
-  const uint16_t* sx16 = reinterpret_cast<const uint16_t*>(p.sx);
+  // every span is below 2 GiB (checked on the host), so 32-bit offsets
+  const __amdgpu_buffer_rsrc_t rwq = __builtin_amdgcn_make_buffer_rsrc((void*)p.wq, 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rxq = __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)p.sw, 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)p.sx, 0, -1, 0x00020000);
+  const int vcode = lane * 16;            // 16-byte fragment piece of this lane
+  const int vsw = q * 16;                 // this lane's 4 columns x 2 groups of weight scales
+  const int vsx = (lane & 15) * 4;        // this lane's token, both groups
 
   // one step's raw operands: 4 weight and 4 token fragments (both 64-groups),
   // the weight scales of 4 x 4 columns x 2 groups, the token scales (2 groups)
@@ -546,13 +568,13 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   };
   auto load = [&](Ops& o, int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.a[i] = wq[((nt0 + i) * nsteps + s) * 64 + lane];
+    for (int i = 0; i < 4; ++i) o.a[i] = __builtin_amdgcn_raw_buffer_load_b128(rwq, vcode, ((nt0 + i) * nsteps + s) * 1024, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.b[j] = xq[((mt0 + j) * nsteps + s) * 64 + lane];
+    for (int j = 0; j < 4; ++j) o.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rxq, vcode, ((mt0 + j) * nsteps + s) * 1024, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.sw[i] = *reinterpret_cast<const u32x4*>(sw16 + ((((nt0 + i) * nsteps + s) * 4 + q) * 2) * 4);
+    for (int i = 0; i < 4; ++i) o.sw[i] = __builtin_amdgcn_raw_buffer_load_b128(rsw, vsw, ((nt0 + i) * nsteps + s) * 64, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.sx[j] = *reinterpret_cast<const unsigned*>(sx16 + (((mt0 + j) * nsteps + s) * 16 + (lane & 15)) * 2);
+    for (int j = 0; j < 4; ++j) o.sx[j] = __builtin_amdgcn_raw_buffer_load_b32(rsx, vsx, ((mt0 + j) * nsteps + s) * 64, 0);
   };
 
   f32x4 acc[4][4];
@@ -564,18 +586,11 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   auto compute = [&](const Ops& o) {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      float sxf[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sxf[j] = h2f<SVDQ_F16>((o.sx[j] >> (16 * g)) & 0xFFFFu) * (1.0f / 256.0f);
       i32x4 ub[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        // weight scales of this lane's 4 columns 16i + 4q + r in group g
-        float swf[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) swf[r] = h2f<SVDQ_F16>((o.sw[i][g * 2 + (r >> 1)] >> (16 * (r & 1))) & 0xFFFFu);
         const i32x4 ua = widen_nibbles(o.a[i][2 * g], o.a[i][2 * g + 1]);
         // the row's four MFMAs first, so each dequant finds its product done
         i32x4 P[4];
@@ -584,7 +599,11 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(float(P[j][r]), swf[r] * sxf[j], acc[i][j][r]);
+          for (int r = 0; r < 4; ++r) {
+            // weight scale of column 16 i + 4 q + r in group g, token scale of group g
+            const float s = hprod(o.sw[i][g * 2 + (r >> 1)], r & 1, o.sx[j], g, z);
+            acc[i][j][r] = __builtin_fmaf(float(P[j][r]), s, acc[i][j][r]);
+          }
       }
     }
   };
@@ -633,7 +652,8 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[r] = (acc[i][j][r] + lr[i][j][r]) + bv[r];
+          // acc holds 256 x the dequantized sum; acc 2^-8 + lr is one rounding
+          v[r] = __builtin_fmaf(acc[i][j][r], 1.0f / 256.0f, lr[i][j][r]) + bv[r];
           if constexpr (GELU) v[r] = gelu_erf(v[r]);
         }
         *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
@@ -1712,6 +1732,7 @@ K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, con
   const int ra = lowrank ? L->rank_active : 0;
   kp.nchunks = int(svdq::ceil_div(ra, 32));
   kp.nchunks16 = int(svdq::ceil_div(ra, 16));
+  kp.zero = 0.0f;
   return kp;
 }
 
@@ -1734,8 +1755,11 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
 // the MXFP4 GEMM addresses the blob from L2 and the workspace from the
 // activation codes with 31-bit offsets
 bool mx_offsets_fit(const svdq_layer* L, const svdq::WsOffsets& w) {
-  if (L->fmt == SVDQ_FMT_INT4_G64) return true;
   const size_t lim = size_t(1) << 31;
+  if (L->fmt == SVDQ_FMT_INT4_G64) {
+    // the INT4 GEMM's buffer loads: codes and scales of each operand
+    return size_t(L->N) * size_t(L->K) / 2 < lim && size_t(w.Mp) * size_t(L->K) / 2 < lim;
+  }
   return L->off_bias + size_t(L->N) * 4 - L->off_l2 < lim && w.total - w.xq < lim;
 }
 
