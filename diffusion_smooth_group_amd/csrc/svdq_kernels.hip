@@ -43,6 +43,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int MAXJT = SVDQ_MAX_RANK_CAPACITY / 16;   // 16-rank tiles of T
 
@@ -483,7 +484,6 @@ struct K2Params {
   uint16_t* Y;
   int64_t ldy, M, N, K;
   int slots, nchunks, nchunks16;
-  float zero;   // 0.0f, passed at run time (the INT4 scale products use it)
 };
 
 __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
@@ -516,40 +516,31 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return x < 0.0f ? h : x - h;
 }
 
-// Exact product of two fp16 scales, each the low or high half of a word, as
-// one v_fma_mix_f32 (the f16 operands are widened inside the instruction).
-// z is a runtime zero: with a literal 0 the compiler drops the addend and
-// emits two conversions and a multiply instead.  The product of two fp16
-// values is exact in fp32, so this equals float(a) * float(b).
-__device__ __forceinline__ float hprod(unsigned a, int ha, unsigned b, int hb, float z) {
-  const _Float16 x = __builtin_bit_cast(_Float16, (unsigned short)(ha ? a >> 16 : a & 0xFFFFu));
-  const _Float16 y = __builtin_bit_cast(_Float16, (unsigned short)(hb ? b >> 16 : b & 0xFFFFu));
-  return __builtin_fmaf((float)x, (float)y, z);
-}
-
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
 // 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per 64-group the
 // integer MFMA gives the exact partial P_g (the nibbles are widened to
-// 16 q per byte, so the MFMA sums 256 P_g); it is dequantized on the VALU
-// into fp32 accumulators: acc += f32(256 P) * (s_w * s_x), and the epilogue
-// takes the factor 2^-8 back out (exact: scaling by a power of two commutes
-// with every rounding on the way).  Per accumulator and group that is three
-// VALU instructions (scale product, conversion, fused multiply-add), which
-// bound the kernel; so the accumulators live in VGPRs, operands and scales
-// are buffer loads with the lane's offset fixed and the step's offset in
-// scalar registers (no per-step address arithmetic on the VALU), each step
-// loaded one step ahead, and two waves share a SIMD (one's MFMAs run under
-// the other's VALU work).
+// 16 q per byte, so the MFMA sums 256 P_g); it is dequantized into fp32
+// accumulators: acc += f32(256 P) * (s_w * s_x), and the epilogue takes the
+// factor 2^-8 back out (exact: scaling by a power of two commutes with every
+// rounding on the way).  The scale products come from the matrix core: a
+// 16 x 16 x 16 fp16 MFMA whose operands hold only s_w (rows) and s_x
+// (columns) at one k forms the 16 x 16 outer product in the accumulator
+// layout of P, exactly (two fp16 values multiply exactly in fp32, the other
+// terms are zero).  That leaves two VALU instructions per accumulator and
+// group (convert, fused multiply-add).  The accumulators live in VGPRs,
+// operands and scales are buffer loads with the lane's offset fixed and the
+// step's offset in scalar registers (no per-step address arithmetic on the
+// VALU), each step loaded one step ahead, and several waves share a SIMD.
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4;
+  const bool k0 = lane < 16;             // lanes that carry k = 0..3 of a 16 x 16 x 16 operand
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
   const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
   const int nt0 = int(n0 / 16), mt0 = int(m0 / 16);
   const int nsteps = int(p.K / KSTEP);
-  const float z = p.zero;
 
   // every span is below 2 GiB (checked on the host), so 32-bit offsets
   const __amdgpu_buffer_rsrc_t rwq = __builtin_amdgcn_make_buffer_rsrc((void*)p.wq, 0, -1, 0x00020000);
@@ -557,14 +548,13 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)p.sw, 0, -1, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsx = __builtin_amdgcn_make_buffer_rsrc((void*)p.sx, 0, -1, 0x00020000);
   const int vcode = lane * 16;            // 16-byte fragment piece of this lane
-  const int vsw = q * 16;                 // this lane's 4 columns x 2 groups of weight scales
-  const int vsx = (lane & 15) * 4;        // this lane's token, both groups
+  const int vsc = (lane & 15) * 4;        // this lane's column / token: both groups' fp16 scales
 
-  // one step's raw operands: 4 weight and 4 token fragments (both 64-groups),
-  // the weight scales of 4 x 4 columns x 2 groups, the token scales (2 groups)
+  // one step's raw operands: 4 weight and 4 token fragments (both 64-groups)
+  // and the scale dwords (both groups) of the lane's weight column and token
   struct Ops {
-    u32x4 a[4], b[4], sw[4];
-    unsigned sx[4];
+    u32x4 a[4], b[4];
+    unsigned sw[4], sx[4];
   };
   auto load = [&](Ops& o, int s) {
 #pragma unroll
@@ -572,9 +562,9 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) o.b[j] = __builtin_amdgcn_raw_buffer_load_b128(rxq, vcode, ((mt0 + j) * nsteps + s) * 1024, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o.sw[i] = __builtin_amdgcn_raw_buffer_load_b128(rsw, vsw, ((nt0 + i) * nsteps + s) * 64, 0);
+    for (int i = 0; i < 4; ++i) o.sw[i] = __builtin_amdgcn_raw_buffer_load_b32(rsw, vsc, ((nt0 + i) * nsteps + s) * 64, 0);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) o.sx[j] = __builtin_amdgcn_raw_buffer_load_b32(rsx, vsx, ((mt0 + j) * nsteps + s) * 64, 0);
+    for (int j = 0; j < 4; ++j) o.sx[j] = __builtin_amdgcn_raw_buffer_load_b32(rsx, vsc, ((mt0 + j) * nsteps + s) * 64, 0);
   };
 
   f32x4 acc[4][4];
@@ -584,26 +574,36 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const Ops& o) {
+    // scale-MFMA operands: A row n holds (s_w[n][g0], s_w[n][g1]) at k = 0, 1;
+    // B column m holds s_x[m][g] at k = g, so A B = s_w[n][g] s_x[m][g]
+    f16x4 sa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sw[i] : 0u, 0u});
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       i32x4 ub[4];
+      f16x4 sb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
+      for (int j = 0; j < 4; ++j) {
+        ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
+        sb[j] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sx[j] & (g ? 0xFFFF0000u : 0x0000FFFFu) : 0u, 0u});
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const i32x4 ua = widen_nibbles(o.a[i][2 * g], o.a[i][2 * g + 1]);
-        // the row's four MFMAs first, so each dequant finds its product done
+        // the row's integer MFMAs and scale products first, so each dequant
+        // finds its operands done
         i32x4 P[4];
+        f32x4 S[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) P[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          P[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          S[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(sa[i], sb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // weight scale of column 16 i + 4 q + r in group g, token scale of group g
-            const float s = hprod(o.sw[i][g * 2 + (r >> 1)], r & 1, o.sx[j], g, z);
-            acc[i][j][r] = __builtin_fmaf(float(P[j][r]), s, acc[i][j][r]);
-          }
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(float(P[j][r]), S[j][r], acc[i][j][r]);
       }
     }
   };
@@ -1732,7 +1732,6 @@ K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, con
   const int ra = lowrank ? L->rank_active : 0;
   kp.nchunks = int(svdq::ceil_div(ra, 32));
   kp.nchunks16 = int(svdq::ceil_div(ra, 16));
-  kp.zero = 0.0f;
   return kp;
 }
 

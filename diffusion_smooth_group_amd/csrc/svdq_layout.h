@@ -31,7 +31,7 @@ constexpr int FRAG_BYTES = 1024;   // 64 lanes x 16 bytes
 constexpr int M_PAD = 256;         // workspace rows are padded to this
 constexpr int HDR_BYTES = 256;
 constexpr uint32_t BLOB_MAGIC = 0x51445653u;   // "SVDQ"
-constexpr uint32_t BLOB_VERSION = 2u;
+constexpr uint32_t BLOB_VERSION = 3u;
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -133,10 +133,12 @@ inline size_t mx_scale_pos(int64_t r, int64_t b, int64_t K) {
 }
 
 // INT4 fp16 scale of weight (column n, 64-group G): element (uint16) offset.
-// Per (16-column tile, step): [q = (n%16)/4][group in step][n % 4].
+// Per (16-column tile, step): [n % 16][group in step], so one dword holds a
+// column's two scales of the step, low half first (the GEMM's scale MFMA
+// takes that dword as its k = 0, 1 operand).
 inline size_t int4_wscale_pos(int64_t n, int64_t G, int64_t K) {
-  int64_t t = n / 16, s = G / 2, g = G % 2, q = (n % 16) / 4, i = n % 4;
-  return size_t((((t * (K / KSTEP) + s) * 4 + q) * 2 + g) * 4 + i);
+  int64_t t = n / 16, s = G / 2, g = G % 2;
+  return size_t(((t * (K / KSTEP) + s) * 16 + n % 16) * 2 + g);
 }
 
 // INT4 fp16 scale of activation (token m, 64-group G): element offset.

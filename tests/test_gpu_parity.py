@@ -104,6 +104,20 @@ def test_token_counts(M):
     G.run_layer_case(d, o.INT4, 8)
 
 
+@pytest.mark.parametrize("fmt", [o.INT4, o.MXFP4])
+def test_tiny_values_subnormal_scales(fmt):
+    # X and W scaled by 2^-14 (exact in bf16), the bias by 2^-28: the INT4
+    # group scales absmax / 7 land in fp16's subnormal range on both sides,
+    # which the scale products must keep (no flush to zero)
+    d = dict(_small(96, 512, 256, o.BF16, fmt, 16, seed=7))
+    for key, sc in (("X", 2.0 ** -14), ("W", 2.0 ** -14), ("bias", 2.0 ** -28)):
+        d[key] = o.round16(o.decode16(d[key], o.BF16) * sc, o.BF16)
+    lin, res = G.run_layer_case(d, fmt, 16)
+    if fmt == o.INT4:
+        sx = o.decode16(lin.workspace_export(96)["scales"], o.F16)
+        assert np.mean((sx > 0) & (sx < 2.0 ** -14)) > 0.5, "most activation scales should be fp16 subnormals"
+
+
 def test_rank_zero_is_w4a4():
     d = _small(64, 256, 256, o.BF16, o.MXFP4, 0, seed=5)
     G.run_layer_case(d, o.MXFP4, 0, cap=0)
