@@ -170,9 +170,11 @@ svdq_status svdq_workspace_size(const svdq_layer* layer, int64_t M, size_t* byte
  * optional GELU in its epilogue.  X_dev: M x K (ldx >= K, ldx % 8 == 0,
  * 16-byte aligned); Y_dev: M x N (ldy >= N, ldy % 8 == 0, 16-byte aligned);
  * ws_dev: >= svdq_workspace_size bytes, 256-byte aligned.  M >= 0 (M == 0
- * is a no-op).  MXFP4 layers: SVDQ_ERR_UNSUPPORTED if the workspace or the
- * blob's span from L2 to the bias reaches 2 GiB (the GEMM addresses them
- * with 31-bit offsets).  Asynchronous. */
+ * is a no-op).  SVDQ_ERR_UNSUPPORTED if an operand span the GEMM addresses
+ * with 31-bit offsets reaches 2 GiB: MXFP4 and INT8, the workspace or the
+ * blob's span from L2 to the bias; INT4, the weight codes (N K / 2 bytes)
+ * or the activation codes (M rounded up to 256, times K / 2 bytes).
+ * Asynchronous. */
 svdq_status svdq_linear_forward(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
                                 void* Y_dev, int64_t ldy, void* ws_dev, size_t ws_bytes, unsigned flags,
                                 hipStream_t stream);
