@@ -496,13 +496,18 @@ __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
 // GELU in its exact form x Phi(x), written without branches so an epilogue
 // over many accumulators stays straight-line code.  With a = |x| and
 // E(a) = erfc(a / sqrt2) / 2 (the Gaussian tail), GELU(x) = x - x E(a) for
-// x >= 0 and x E(a) for x < 0.  E(a) = 2^(-a^2 log2(e) / 2 + N(a)) where N, a
+// x >= 0 and x E(a) for x < 0, i.e. max(x, 0) - |x| E(a) in both cases (one
+// fused multiply-add).  E(a) = 2^(-a^2 log2(e) / 2 + N(a)) where N, a
 // degree-7 polynomial fitted to log2(erfcx(a / sqrt2) / 2) on [0, 4 sqrt2]
 // (fit_gelu.py beside this file; a is clamped there), keeps the relative
-// error of E, and of GELU, below 6e-6 in float32: one exp2 and eight fused
-// multiply-adds per element.
+// error of E, and of GELU, below 6e-6 in float32: one exp2 and ten other
+// VALU instructions per element.  (Degree 6, at 3e-5, moves enough fp16
+// roundings of an fc1 output that fc2's 4-bit codes of a few elements flip.)
 __device__ __forceinline__ float gelu_erf(float x) {
-  const float a = fminf(fabsf(x), 5.656854249f);
+  // clamp and max(x, 0) as v_med3_f32: fminf / fmaxf would first quiet
+  // their inputs with an extra instruction each (a NaN x still yields NaN
+  // through the last multiply-add)
+  const float a = __builtin_amdgcn_fmed3f(fabsf(x), 0.0f, 5.656854249f);
   float p = -1.8169505645e-06f;
   p = __builtin_fmaf(p, a, 6.1296118065e-05f);
   p = __builtin_fmaf(p, a, -9.2855348124e-04f);
@@ -512,8 +517,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
   p = __builtin_fmaf(p, a, -1.1512491604e+00f);
   p = __builtin_fmaf(p, a, -9.9999537112e-01f);
   const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(a * -0.72134752044f, a, p));   // E(a)
-  const float h = x * e;
-  return x < 0.0f ? h : x - h;
+  return __builtin_fmaf(-fabsf(x), e, __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f));   // max(x, 0)
 }
 
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
