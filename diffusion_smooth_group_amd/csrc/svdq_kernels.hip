@@ -1617,6 +1617,7 @@ template <int DT>
 void launch_k1_w8(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
   if (kp.njt == 0) hipLaunchKernelGGL((k1_w8<DT, 0>), grid, block, 0, st, kp);
+  else if (kp.njt == 1) hipLaunchKernelGGL((k1_w8<DT, 1>), grid, block, 0, st, kp);
   else if (kp.njt <= 2) hipLaunchKernelGGL((k1_w8<DT, 2>), grid, block, 0, st, kp);
   else if (kp.njt <= 4) hipLaunchKernelGGL((k1_w8<DT, 4>), grid, block, 0, st, kp);
   else hipLaunchKernelGGL((k1_w8<DT, MAXJT>), grid, block, 0, st, kp);
@@ -1690,9 +1691,11 @@ void run_k1(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx, uint
   kp.invlam = reinterpret_cast<const float*>(blob + L->off_invlam);
   kp.l1x = reinterpret_cast<const uint16_t*>(blob + L->off_l1x);
   kp.slots = L->rank_slots;
+  // 16-column tiles of T: INT4 fills whole 32-rank chunks (its L1x and T
+  // tiling); the MX low-rank layout (MXFP4 and INT8) takes single tiles
   kp.njt = mode == K1_QUANT ? 0
-           : L->fmt == SVDQ_FMT_MXFP4_G32 ? int(svdq::ceil_div(L->rank_active, 16))
-                                         : 2 * int(svdq::ceil_div(L->rank_active, 32));
+           : L->fmt == SVDQ_FMT_INT4_G64 ? 2 * int(svdq::ceil_div(L->rank_active, 32))
+                                         : int(svdq::ceil_div(L->rank_active, 16));
   kp.xq = ws + w.xq; kp.sx = ws + w.sx; kp.t = reinterpret_cast<uint16_t*>(ws + w.t);
   if (L->fmt == SVDQ_FMT_INT8_W8A8) {
     // one kernel for codes, scales and T (the separate-pass modes are not built for INT8)
