@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
           unsigned v = 0u;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float rc = fminf(fmaxf(r[cc][e], -7.0f), 7.0f);
+            const float rc = __builtin_amdgcn_fmed3f(r[cc][e], -7.0f, 7.0f);   // clamp, one v_med3_f32
             v |= (unsigned(int(rc)) & 0xFu) << (4 * e);
           }
           d[2 * g + cc] = v;
@@ -808,7 +808,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
       unsigned d[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float rc = fminf(fmaxf(r[e], -127.0f), 127.0f);
+        const float rc = __builtin_amdgcn_fmed3f(r[e], -127.0f, 127.0f);   // clamp, one v_med3_f32
         d[e >> 2] |= (unsigned(int(rc)) & 0xFFu) << (8 * (e & 3));
       }
       // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, half c % 2, lane
