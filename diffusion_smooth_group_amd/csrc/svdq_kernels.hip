@@ -92,14 +92,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 #define SVDQ_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xF | (3 << 14) | (0x7 << 4))
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* glb_ptr_t;
-
-__device__ __forceinline__ void lds_load16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
-}
 
 // Max of a non-negative float over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four
 // lanes q = 0..3 of one token in the activation kernel).  permlane16_swap
@@ -135,12 +127,6 @@ __device__ __forceinline__ int e8m0_slow(float a) {      // any a >= 0
 }
 __device__ __forceinline__ bool e8m0_needs_slow(float a) { return (__float_as_uint(a) >> 23) < 3u; }
 
-// E2M1 magnitude index of a >= 0: nearest value, ties to the even mantissa, saturating at 6.
-__device__ __forceinline__ unsigned e2m1_index(float a) {
-  return unsigned(a > 0.25f) + unsigned(a >= 0.75f) + unsigned(a > 1.25f) + unsigned(a >= 1.75f) +
-         unsigned(a > 2.5f) + unsigned(a >= 3.5f) + unsigned(a > 5.0f);
-}
-
 // ------------------------------------------------------------------- k1_act
 struct K1Params {
   const uint16_t* X;
@@ -154,10 +140,12 @@ struct K1Params {
 };
 
 // One workgroup = 16 tokens; its 4 waves take the 128-deep K steps round
-// robin.  Lane l = m + 16q holds token m and, in chunk c = 0..3 of a step,
-// k in [32c + 8q, 32c + 8q + 8): the four lanes of a token read 64
-// contiguous bytes per load instruction.  An MXFP4 block (32 k) is chunk c
-// of lanes q = 0..3; an INT4 64-group is chunks 2g and 2g + 1 of those lanes.
+// robin, and lane l = m + 16q holds token m.  MXFP4: lane group q holds the
+// whole 32-block q of a step (four 16-byte loads of consecutive k), so the
+// block maximum, exponent and codes are the lane's own work.  INT4: in
+// chunk c = 0..3 of a step the lane holds k in [32c + 8q, 32c + 8q + 8) (the
+// four lanes of a token read 64 contiguous bytes per load instruction), so
+// a 64-group is chunks 2g and 2g + 1 of the token's four lanes.
 //
 // Latency.  The vector memory counter retires in issue order, so waiting for
 // a short (L2) load also waits for every older HBM load.  Each step is
