@@ -648,7 +648,8 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
           v[r] = __builtin_fmaf(acc[i][j][r], 1.0f / 256.0f, lr[i][j][r]) + bv[r];
           if constexpr (GELU) v[r] = gelu_erf(v[r]);
         }
-        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+        __builtin_nontemporal_store(u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])},
+                                    reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n));   // streamed out
       }
     }
   }
@@ -1370,12 +1371,15 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     SVDQ_WAIT_LGKM0();
     const int64_t mw = m0 + 128 * wm;      // first token of this wave's tile
     if (nw < p.N && (!CHAIN || p.Y != nullptr)) {
+      // non-temporal stores: Y is not read again here, and streaming it out
+      // leaves fewer dirty lines for the next kernel's reads to wait behind
 #pragma unroll 4
       for (int it = 0; it < 32; ++it) {
         const int row = 4 * it + (lane >> 4);
         const int col = (lane & 15) * 8;
         const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
-        if (mw + row < p.M) *reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col) = val;
+        if (mw + row < p.M)
+          __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col));
       }
     }
     if constexpr (CHAIN) chain_epilogue<DT>(p, smem, ob, wave, lane, m0, n0, nw, mw);
