@@ -12,8 +12,8 @@ Default workload: the FLUX.1-shaped MLP fc1 linear at 1024^2 (4608 tokens x
 3072 -> 12288), bf16 activations, MXFP4 group 32 with e8m0 scales, rank 32.
 Metric: effective TOPS = 2 M K N / t (the low-rank FLOPs are not counted).
 
-Prints one JSON line.  The CPU baseline is the CPU oracle's float32 forward
-timed on a bounded sample of the same layer, on this host's cores.
+Prints one JSON line.  The CPU baseline is the CPU oracle's own float64
+forward timed on a bounded sample of the same layer, on this host's cores.
 """
 from __future__ import annotations
 

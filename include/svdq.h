@@ -42,7 +42,7 @@ typedef enum {
   SVDQ_OK = 0,
   SVDQ_ERR_INVALID_ARG = 1,  /* null pointer, bad enum, negative size, bad rank */
   SVDQ_ERR_SHAPE = 2,        /* K not a multiple of 128, N of 128, strides too small */
-  SVDQ_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement */
+  SVDQ_ERR_UNSUPPORTED = 3,  /* valid request the library does not implement */
   SVDQ_ERR_CAPACITY = 4,     /* buffer too small, LoRA rank beyond the capacity */
   SVDQ_ERR_NUMERIC = 5,      /* non-finite weights or calibration maxima */
   SVDQ_ERR_HIP = 6           /* a HIP runtime call or kernel launch failed */
