@@ -648,8 +648,7 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
           v[r] = __builtin_fmaf(acc[i][j][r], 1.0f / 256.0f, lr[i][j][r]) + bv[r];
           if constexpr (GELU) v[r] = gelu_erf(v[r]);
         }
-        __builtin_nontemporal_store(u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])},
-                                    reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n));   // streamed out
+        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
       }
     }
   }
