@@ -633,24 +633,35 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) lr[i][j] = mfma16<DT>(la[i], tb[j], lr[i][j]);
   }
+  // the wave's 64 x 64 tile goes through LDS as [token][column] rows so the
+  // global stores cover whole 128-byte lines (non-temporal: Y is not read
+  // again here)
+  constexpr int OP = 64 * 2 + 16;                       // bytes per staged row
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[4][64 * OP];
+  uint8_t* ob = ostage[wave];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t n = n0 + 16 * i + 4 * q;
-    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n);
+    const f32x4 bv = *reinterpret_cast<const f32x4*>(p.bias + n0 + 16 * i + 4 * q);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + 16 * j + (lane & 15);
-      if (m < p.M) {
-        float v[4];
+      float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // acc holds 256 x the dequantized sum; acc 2^-8 + lr is one rounding
-          v[r] = __builtin_fmaf(acc[i][j][r], 1.0f / 256.0f, lr[i][j][r]) + bv[r];
-          if constexpr (GELU) v[r] = gelu_erf(v[r]);
-        }
-        *reinterpret_cast<u32x2*>(p.Y + m * p.ldy + n) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+      for (int r = 0; r < 4; ++r) {
+        // acc holds 256 x the dequantized sum; acc 2^-8 + lr is one rounding
+        v[r] = __builtin_fmaf(acc[i][j][r], 1.0f / 256.0f, lr[i][j][r]) + bv[r];
+        if constexpr (GELU) v[r] = gelu_erf(v[r]);
       }
+      *reinterpret_cast<u32x2*>(ob + (16 * j + (lane & 15)) * OP + (16 * i + 4 * q) * 2) =
+          u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
     }
+  }
+  SVDQ_WAIT_LGKM0();
+  // 8 rows of 128 bytes per instruction: lane l takes row l / 8, piece l % 8
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int row = 8 * it + (lane >> 3), col = (lane & 7) * 8;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OP + col * 2);
+    if (m0 + row < p.M) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col));
   }
 }
 
