@@ -11,6 +11,7 @@ import oracle
 import oracle.svdquant as osq
 from tests import test_oracle_quant as tq
 from tests import test_oracle_split as ts
+from tests import test_oracle_gelu_lora as tg
 
 
 def _patch(monkeypatch, name, fn):
@@ -118,3 +119,56 @@ def test_mutant_int4_partial_sign(monkeypatch):
     _patch(monkeypatch, "int4_group_partials", bad)
     _expect_fail((ts.test_brute_force_tiny, (oracle.INT4, 128, oracle.F16)),
                  (ts.test_rank0_unit_lambda_is_naive_w4a4, ()))
+
+
+_GELU_PINS = ((tg.test_gelu_closed_values, ()), (tg.test_gelu_matches_quadrature_of_the_density, ()),
+              (tg.test_gelu_odd_part_is_identity, ()), (tg.test_gelu_slope_at_zero_and_derivative, ()),
+              (tg.test_gelu_tails, ()))
+
+
+def test_mutant_gelu_tanh_form(monkeypatch):
+    def bad(x):
+        x = np.asarray(x, np.float64)
+        return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    _patch(monkeypatch, "gelu_erf", bad)
+    _expect_fail(*_GELU_PINS)
+
+
+def test_mutant_gelu_wrong_sqrt2(monkeypatch):
+    from scipy.special import erf
+
+    def bad(x):
+        x = np.asarray(x, np.float64)
+        return 0.5 * x * (1.0 + erf(x / 2.0))
+    _patch(monkeypatch, "gelu_erf", bad)
+    _expect_fail(*_GELU_PINS)
+
+
+def _lora_pins():
+    return tuple((tg.test_lora_adds_exactly_its_own_product_on_raw_x, (a,)) for a in (1.0, 0.3, -1.7)) + \
+        ((tg.test_lora_leaves_residual_and_branch_untouched, ()),)
+
+
+def test_mutant_lora_alpha_on_a(monkeypatch):
+    def bad(layer, A_bits, B_bits, alpha=1.0):
+        dt = layer["dtype"]
+        A, B = osq.decode16(A_bits, dt), osq.decode16(B_bits, dt)
+        out = dict(layer)
+        out["L1x"] = np.concatenate([layer["L1x"], osq.round16(float(alpha) * A, dt)], axis=1)
+        out["L2q"] = np.concatenate([layer["L2q"], osq.round16(B, dt)], axis=0)
+        return out
+    _patch(monkeypatch, "attach_lora", bad)
+    _expect_fail(*_lora_pins())
+
+
+def test_mutant_lora_on_smoothed_input(monkeypatch):
+    def bad(layer, A_bits, B_bits, alpha=1.0):
+        dt = layer["dtype"]
+        A, B = osq.decode16(A_bits, dt), osq.decode16(B_bits, dt)
+        out = dict(layer)
+        Ah = np.asarray(layer["invlam"], np.float64)[:, None] * A     # LoRA applied to X_hat
+        out["L1x"] = np.concatenate([layer["L1x"], osq.round16(Ah, dt)], axis=1)
+        out["L2q"] = np.concatenate([layer["L2q"], osq.round16(float(alpha) * B, dt)], axis=0)
+        return out
+    _patch(monkeypatch, "attach_lora", bad)
+    _expect_fail(*_lora_pins())
