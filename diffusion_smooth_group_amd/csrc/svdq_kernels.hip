@@ -767,6 +767,9 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   const float tmax = fmaxf(fmaxf(smax[0][m], smax[1][m]), fmaxf(smax[2][m], smax[3][m]));
   const float sc = tmax / 127.0f;
   const float inv = sc != 0.0f ? 1.0f / sc : 0.0f;
+  // below 2^-128 the reciprocal overflows: such a token takes the division
+  // for every code
+  const bool inv_inf = !(inv <= 3.40282347e38f);
   if (wave == 0 && q == 0) reinterpret_cast<float*>(p.sx)[size_t(mt) * 16 + m] = sc;
   if constexpr (NJT > 0) {
     // T = the four waves' partial sums (fixed order), rounded once, in the
@@ -793,7 +796,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
     for (int c = 0; c < 4; ++c) {
       float xh[8], r[8];
       smooth_c(x[c], s, c, xh);
-      bool near = false;
+      bool near = inv_inf;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float qv = xh[e] * inv;
