@@ -24,6 +24,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "svdq.h"
 #include "svdq_layout.h"
@@ -1944,6 +1945,47 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
     run_up(L, M, Y_dev, ldy, ws, w, gelu, stream);
   }
   return launch_ok();
+}
+
+// ------------------------------------------------- forward without allocation
+// Library-owned workspace for svdq_linear_forward_noalloc: one copy per GPU
+// (each device that loads this code object holds its own), kept until the
+// process ends.  Host code never passes the symbol itself to a kernel: its
+// device address comes from hipGetSymbolAddress, looked up once per device.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[SVDQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// device address of this device's scratch array (looked up on first use)
+svdq_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SVDQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return SVDQ_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVDQ_OK;
+}
+}  // namespace
+
+extern "C" svdq_status svdq_linear_forward_noalloc(const svdq_layer* L, const void* X_dev, int64_t M, int64_t ldx,
+                                                   void* Y_dev, int64_t ldy, unsigned flags, hipStream_t stream) {
+  svdq_status st = check_device_layer(L);
+  if (st != SVDQ_OK) return st;
+  if (M < 0 || (flags & ~SVDQ_FLAGS_ALL) != 0u) return SVDQ_ERR_INVALID_ARG;
+  if (M == 0) return SVDQ_OK;
+  // the workspace this forward needs must fit the library's array
+  const svdq::WsOffsets w = svdq::ws_offsets(M, L->K, L->rank_slots, L->fmt);
+  if (w.total > size_t(SVDQ_NOALLOC_SCRATCH_BYTES)) return SVDQ_ERR_CAPACITY;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != SVDQ_OK) return st;
+  return svdq_linear_forward(L, X_dev, M, ldx, Y_dev, ldy, ws, size_t(SVDQ_NOALLOC_SCRATCH_BYTES), flags, stream);
 }
 
 extern "C" svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int64_t ldx,

@@ -67,6 +67,7 @@ _SIGS = {
     "svdq_detach_lora": [_LP, _P],
     "svdq_workspace_size": [_LP, _I64, C.POINTER(_SZ)],
     "svdq_linear_forward": [_LP, _P, _I64, _I64, _P, _I64, _P, _SZ, C.c_uint, _P],
+    "svdq_linear_forward_noalloc": [_LP, _P, _I64, _I64, _P, _I64, C.c_uint, _P],
     "svdq_quantize_activations": [_LP, _P, _I64, _I64, _P, _SZ, _P],
     "svdq_gemm_forward": [_LP, _I64, _P, _I64, _P, _SZ, C.c_uint, _P],
     "svdq_activation_absmax": [_P, _I64, _I64, _I64, _I, _P, _P],

@@ -19,7 +19,9 @@
  *     the ABI.  Argument and shape errors are reported synchronously before
  *     anything is launched.
  *   - All device memory (packed blob, X, Y, workspace) is allocated and owned
- *     by the caller.  The library never allocates device memory.
+ *     by the caller.  The library never allocates device memory; the one
+ *     exception, svdq_linear_forward_noalloc, uses a fixed array that is part
+ *     of the library's device code object.
  *   - Row-major storage.  X is M x K with row stride ldx elements, Y is
  *     M x N with row stride ldy elements, both in the layer's 16-bit dtype.
  *   - Host buffers passed to synchronous calls may be freed on return.
@@ -178,6 +180,23 @@ svdq_status svdq_workspace_size(const svdq_layer* layer, int64_t M, size_t* byte
 svdq_status svdq_linear_forward(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
                                 void* Y_dev, int64_t ldy, void* ws_dev, size_t ws_bytes, unsigned flags,
                                 hipStream_t stream);
+
+/* svdq_linear_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the workspace is a library-owned device array of
+ * SVDQ_NOALLOC_SCRATCH_BYTES per GPU (each GPU the library runs on holds it
+ * until the process ends).  Same arguments, kernels and results as
+ * svdq_linear_forward, minus ws_dev / ws_bytes.  Calls no allocating routine.
+ * SVDQ_ERR_CAPACITY if svdq_workspace_size(layer, M) exceeds the array (32 MiB
+ * covers the 4-bit formats at 4608 tokens with K up to 12288 and rank
+ * capacity 128).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (several streams, or several host threads) race and must be serialised
+ * by the caller.  Nothing in the array needs to start at zero (each kernel
+ * writes what the next reads).  Asynchronous. */
+#define SVDQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+svdq_status svdq_linear_forward_noalloc(const svdq_layer* layer, const void* X_dev, int64_t M, int64_t ldx,
+                                        void* Y_dev, int64_t ldy, unsigned flags, hipStream_t stream);
 
 /* The two stages of svdq_linear_forward, callable on their own (the second
  * reads what the first wrote into ws_dev).  Asynchronous. */
