@@ -879,6 +879,7 @@ struct MxParams {
   int64_t ldy, M, N, K;
   int slots, nchunks16;
   int tiles_n, tiles_m;
+  int tiles_m_pad32;     // 32-row token tiles in the workspace (its padded rows / 32)
   // byte offsets of the weight-side regions from l2 (all in the layer blob)
   // and of the token-side regions from xq (all in the workspace); both spans
   // are below 2 GiB, so the stage loads take them as scalar offsets
@@ -1400,6 +1401,418 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   }
 }
 
+// ---------------------------------------- k2_mx8 (MXFP4, two waves per SIMD)
+// The MXFP4 GEMM with two waves on every SIMD, so one wave's LDS reads,
+// waits and barrier stalls (and its epilogue) run under another's MFMAs.  A
+// workgroup = WN x WM waves, each TI x TJ tiles of 32 x 32 on
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4; four-wave workgroups run two to a
+// compute unit (the 192 x 192 tile in use), eight-wave ones alone.  A K step
+// is taken in its two 64-deep halves: the MFMAs of one half run while the
+// fragments of the other half (and of the next step) are read from LDS, so
+// a wave holds one half-step of fragments twice over instead of a whole step
+// twice over (144 accumulators and 48 fragment registers fit the 256 a wave
+// has at two waves per SIMD).  Stages: a ring of K steps filled by buffer
+// loads straight into LDS; after the per-step barrier the stage of the step
+// just finished is refilled with the step STAGES ahead.  Every wave issues
+// the same number of stage loads per step (so one immediate s_waitcnt count
+// fits all waves): the fragment halves are dealt out first, then the e8m0
+// pair dwords, the spare slots repeating the last pair.  The steady-state
+// step has no branches (the compiler keeps the MFMA / memory interleave of
+// a single basic block); the last steps, which may request low-rank steps,
+// take a branchy path.  Bias, the low-rank up-projection and the epilogue
+// (GELU, rounding, row-staged non-temporal stores) are as in k2_mx; the
+// whole workgroup tile is staged at once.
+namespace mx8 {
+constexpr int scale_slots_low(int FR, int S, int NW) {
+  int sl = 0;
+  while (FR * sl + (NW - FR) * (sl + 1) < S) ++sl;
+  return sl;
+}
+template <int WN_, int WM_, int TI_, int TJ_, int STAGES_ = 4>
+struct Cfg {
+  static constexpr int WN = WN_, WM = WM_, TI = TI_, TJ = TJ_;
+  static constexpr int NW = WN * WM;                        // waves per workgroup
+  static_assert(NW == 8 || NW == 4, "four or eight waves");
+  static constexpr int NT = WN * TI, MT = WM * TJ;          // 32-row tiles of the workgroup tile
+  static constexpr int TN = 32 * NT, TM = 32 * MT;
+  static constexpr int NPA = (NT + 1) / 2, NPB = (MT + 1) / 2;   // e8m0 dword pairs per step
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = NT * 2048;
+  static constexpr int SA_OFF = B_OFF + MT * 2048;
+  static constexpr int SB_OFF = SA_OFF + NPA * 256;
+  static constexpr int STAGE = SB_OFF + NPB * 256;
+  static constexpr int STAGES = STAGES_;
+  static_assert(STAGES == 3 || STAGES == 4, "stage ring");
+  // workgroups per compute unit: eight-wave tiles fill a CU alone, four-wave
+  // tiles run two to a CU (two waves per SIMD either way)
+  static constexpr int WG_PER_CU = NW == 8 ? 1 : 2;
+  // stage loads per step: F fragment halves (1 KB each), S pair dwords (256 B
+  // each); waves below FR take FQ + 1 fragment halves and SL pairs, the
+  // others FQ halves and SL + 1 pairs
+  static constexpr int F = 2 * NT + 2 * MT, S = NPA + NPB;
+  static constexpr int FQ = F / NW, FR = F % NW;
+  static constexpr int SL = scale_slots_low(FR, S, NW);
+  static constexpr int LPW = FQ + SL + 1;
+  static constexpr int PITCH = TN * 2 + 16;                   // staged output row bytes
+  static constexpr int LDS = STAGES * STAGE > TM * PITCH ? STAGES * STAGE : TM * PITCH;
+};
+// 192 x 192, two workgroups per compute unit (the one in use, for layers
+// with a GELU epilogue: one workgroup's epilogue runs under the other's K
+// loop); 384 x 192 and 256 x 256 eight-wave tiles were measured too
+using Pair = Cfg<2, 2, 3, 3, 3>;
+static_assert(Pair::LDS <= 80 * 1024, "two workgroups per compute unit");
+static_assert(Pair::FR == 0 && Pair::SL == 1 && Pair::LPW == 8, "load classes");
+}  // namespace mx8
+
+// One wave's share of a workgroup tile.  PA / PB: parity of the wave's first
+// weight / token tile in the workgroup tile (it fixes where each tile's e8m0
+// bytes sit in the pair dwords, byte 2 (tile % 2) + half); CLS: the wave's
+// load class (0: one more fragment half, one pair dword fewer).
+template <int DT, bool GELU, class C, int PA, int PB, int CLS>
+__device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int wave, int lane, int64_t n0, int64_t m0) {
+  constexpr int TI = C::TI, TJ = C::TJ, LPW = C::LPW;
+  constexpr int NF = CLS == 0 ? C::FQ + 1 : C::FQ;                         // fragment slots
+  constexpr int NSA = (PA + TI - 1) / 2 + 1, NSB = (PB + TJ - 1) / 2 + 1;   // pair dwords read per side
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  const int ia0 = wn * TI, jb0 = wm * TJ;              // first tile of the wave in the workgroup tile
+  const int nsteps = int(p.K / KSTEP);
+  const int64_t ntiles_n = p.N / 32;
+  const int64_t ntiles_m = p.tiles_m_pad32;            // 32-row token tiles in the workspace
+  const int cs = p.slots / 16;
+  const int nk = nsteps;
+  const int total = nk + (p.nchunks16 + 1) / 2;
+
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc((void*)p.l2, 0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsw = __builtin_amdgcn_make_buffer_rsrc((void*)p.xq, 0, -1, 0x00020000);
+  const int lo16 = lane * 16, lo4 = lane * 4;
+
+  // ---- this wave's stage loads (uniform): source offset of K step 0, source
+  // offset of low-rank chunk 0 (fragment slots), LDS offset | half << 20 |
+  // workspace-side << 21
+  int src_k[LPW], src_lr[LPW], info[LPW];
+  {
+    const int f0 = CLS == 0 ? wave * (C::FQ + 1) : C::FR * (C::FQ + 1) + (wave - C::FR) * C::FQ;
+    const int g0 = CLS == 0 ? wave * C::SL : C::FR * C::SL + (wave - C::FR) * (C::SL + 1);
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) {
+      if (k < NF) {
+        const int u = f0 + k;
+        if (u < 2 * C::NT) {
+          const int t = u >> 1, h = u & 1;
+          int64_t nt = n0 / 32 + t;
+          nt = nt < ntiles_n ? nt : ntiles_n - 1;      // a partial last tile re-reads a valid tile
+          src_k[k] = p.off_wq + int(nt * nsteps * 2 + h) * 1024;
+          src_lr[k] = int(nt * cs) * 1024;
+          info[k] = (C::A_OFF + u * 1024) | (h << 20);
+        } else {
+          const int v = u - 2 * C::NT, t = v >> 1, h = v & 1;
+          int64_t mt = m0 / 32 + t;
+          mt = mt < ntiles_m ? mt : ntiles_m - 1;
+          src_k[k] = int(mt * nsteps * 2 + h) * 1024;
+          src_lr[k] = p.off_t + int(mt * cs) * 1024;
+          info[k] = (C::B_OFF + v * 1024) | (h << 20) | (1 << 21);
+        }
+      } else {
+        int g = g0 + (k - NF);
+        g = g < C::S ? g : C::S - 1;                   // the spare slots repeat the last pair
+        if (g < C::NPA) {
+          int64_t pn = n0 / 64 + g;
+          pn = pn < p.N / 64 ? pn : p.N / 64 - 1;
+          src_k[k] = p.off_sw + int(pn * nsteps) * 256;
+          info[k] = C::SA_OFF + g * 256;
+        } else {
+          const int q = g - C::NPA;
+          int64_t pm = m0 / 64 + q;
+          pm = pm < ntiles_m / 2 ? pm : ntiles_m / 2 - 1;
+          src_k[k] = p.off_sx + int(pm * nsteps) * 256;
+          info[k] = (C::SB_OFF + q * 256) | (1 << 21);
+        }
+        src_lr[k] = src_k[k];
+      }
+    }
+  }
+  // slot k of K step r into stage r % 4
+  auto issue_k = [&](int r, int k) {
+    uint8_t* base = smem + (r % C::STAGES) * C::STAGE + (info[k] & 0xFFFFF);
+    const __amdgpu_buffer_rsrc_t rs = (info[k] & (1 << 21)) ? rsw : rsb;
+    if (k < NF) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)base, 16, lo16, src_k[k] + r * 2048, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)base, 4, lo4, src_k[k] + r * 256, 0, 0);
+  };
+  // slot k of step r, a K step or a low-rank step (chunks 2e, 2e + 1 of L2
+  // and T in the fragment slots; the pair slots reload K step 0's)
+  auto issue_any = [&](int r, int k) {
+    if (r < nk) {
+      issue_k(r, k);
+      return;
+    }
+    uint8_t* base = smem + (r % C::STAGES) * C::STAGE + (info[k] & 0xFFFFF);
+    const __amdgpu_buffer_rsrc_t rs = (info[k] & (1 << 21)) ? rsw : rsb;
+    if (k < NF) {
+      int c = 2 * (r - nk) + ((info[k] >> 20) & 1);
+      c = c < p.nchunks16 ? c : p.nchunks16 - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)base, 16, lo16, src_lr[k] + c * 1024, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)base, 4, lo4, src_lr[k], 0, 0);
+    }
+  };
+
+  // ---- fragments: one half-step of each side, twice (halves 0 and 1)
+  u32x4 fa[2][TI], fb[2][TJ];
+  unsigned sa[NSA], sb[NSB], na[NSA], nb[NSB];      // e8m0 pair dwords: current / next step
+  auto rd_a = [&](int st, int h, int i) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(smem + st * C::STAGE + C::A_OFF + ((ia0 + i) * 2 + h) * 1024 + lo16);
+  };
+  auto rd_b = [&](int st, int h, int j) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(smem + st * C::STAGE + C::B_OFF + ((jb0 + j) * 2 + h) * 1024 + lo16);
+  };
+  auto rd_sa = [&](int st, int d) -> unsigned {
+    int q = ia0 / 2 + d;
+    q = q < C::NPA ? q : C::NPA - 1;
+    return *reinterpret_cast<const unsigned*>(smem + st * C::STAGE + C::SA_OFF + q * 256 + lo4);
+  };
+  auto rd_sb = [&](int st, int d) -> unsigned {
+    int q = jb0 / 2 + d;
+    q = q < C::NPB ? q : C::NPB - 1;
+    return *reinterpret_cast<const unsigned*>(smem + st * C::STAGE + C::SB_OFF + q * 256 + lo4);
+  };
+  // read x of the next step's half 0: fragments, then pair dwords
+  constexpr int NRD = TI + TJ + NSA + NSB;
+  auto rd_next = [&](int st, int x) {
+    if (x < TI) fa[0][x] = rd_a(st, 0, x);
+    else if (x < TI + TJ) fb[0][x - TI] = rd_b(st, 0, x - TI);
+    else if (x < TI + TJ + NSA) na[x - TI - TJ] = rd_sa(st, x - TI - TJ);
+    else nb[x - TI - TJ - NSA] = rd_sb(st, x - TI - TJ - NSA);
+  };
+
+  f32x16 acc[TI][TJ];
+  // MFMA (h, i, j) with the e8m0 bytes of tile i / j picked by op_sel
+  auto mfma_hij = [&](int h, int i, int j) {
+    const u32x4 av = fa[h][i], bv = fb[h][j];
+    const i32x8 a = i32x8{int(av[0]), int(av[1]), int(av[2]), int(av[3]), 0, 0, 0, 0};
+    const i32x8 b = i32x8{int(bv[0]), int(bv[1]), int(bv[2]), int(bv[3]), 0, 0, 0, 0};
+    acc[i][j] = mfma_mx32(a, b, acc[i][j], int(sa[(PA + i) / 2]), int(sb[(PB + j) / 2]), 2 * ((PA + i) & 1) + h,
+                          2 * ((PB + j) & 1) + h);
+  };
+
+  // ---- prologue: bias of this wave's columns, the first four stages
+  float bcol[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+    int64_t nb_ = n0 + 32 * (ia0 + i) + (lane & 31);
+    nb_ = nb_ < p.N ? nb_ : p.N - 1;
+    bcol[i] = p.bias[nb_];
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  for (int r = 0; r < C::STAGES && r < total; ++r) {
+#pragma unroll
+    for (int k = 0; k < LPW; ++k) issue_any(r, k);
+  }
+  if (C::STAGES > 3 && total > 3) SVDQ_WAIT_VM(3 * LPW);
+  else if (total > 2) SVDQ_WAIT_VM(2 * LPW);
+  else if (total > 1) SVDQ_WAIT_VM(LPW);
+  else SVDQ_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();
+  {
+    // accumulators start at the bias (see k2_mx)
+    const bool lo = lane < 32;
+    const unsigned one = lo ? (DT == SVDQ_BF16 ? 0x3F80u : 0x3C00u) : 0u;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const unsigned bh = lo ? (pack2<DT>(bcol[i], 0.0f) & 0xFFFFu) : 0u;
+      const u32x4 ab = u32x4{bh | (bh << 16), bh | (bh << 16), 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int jj = j & 3;
+        const u32x4 bj = u32x4{jj == 0 ? one : jj == 1 ? one << 16 : 0u, jj == 2 ? one : jj == 3 ? one << 16 : 0u, 0u, 0u};
+        acc[i][j] = mfma32x16<DT>(ab, bj, f32x16{});
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < NRD; ++x) rd_next(0, x);
+#pragma unroll
+  for (int d = 0; d < NSA; ++d) sa[d] = na[d];
+#pragma unroll
+  for (int d = 0; d < NSB; ++d) sb[d] = nb[d];
+
+  // ---- K steps.  Step r:
+  //  phase A: the half-0 MFMAs, with the half-1 fragments of step r read in
+  //           between;
+  //  phase B: wait for step r + 1 (own loads, then the barrier for all
+  //           waves'), then the half-1 MFMAs with the half-0 fragments and
+  //           pair dwords of step r + 1 read in between, and step r's stage
+  //           refilled with the step STAGES ahead.
+  auto phase_a = [&](int r) {
+    const int st = r % C::STAGES;
+    SVDQ_WAIT_LGKM0();
+#pragma unroll
+    for (int k = 0; k < TI * TJ; ++k) {
+      mfma_hij(0, k / TJ, k % TJ);
+      if (k < TI) fa[1][k] = rd_a(st, 1, k);
+      else if (k < TI + TJ) fb[1][k - TI] = rd_b(st, 1, k - TI);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    SVDQ_WAIT_LGKM0();
+  };
+  auto commit_scales = [&]() {
+#pragma unroll
+    for (int d = 0; d < NSA; ++d) sa[d] = na[d];
+#pragma unroll
+    for (int d = 0; d < NSB; ++d) sb[d] = nb[d];
+  };
+  // steady state (r + STAGES < nk): no branches, the memory operations of
+  // phase B two per MFMA (the reads first, the stage refill after)
+  constexpr int AHEAD = C::STAGES;
+  auto kstep = [&](int r) {
+    phase_a(r);
+    SVDQ_WAIT_VM((C::STAGES - 2) * LPW);
+    __builtin_amdgcn_s_barrier();
+    const int st1 = (r + 1) % C::STAGES;
+#pragma unroll
+    for (int k = 0; k < TI * TJ; ++k) {
+      mfma_hij(1, k / TJ, k % TJ);
+#pragma unroll
+      for (int x = 2 * k; x < 2 * k + 2; ++x) {
+        if (x < NRD) rd_next(st1, x);
+        else if (x - NRD < LPW) issue_k(r + AHEAD, x - NRD);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int x = 2 * TI * TJ; x < NRD + LPW; ++x) {
+      if (x < NRD) rd_next(st1, x);
+      else issue_k(r + AHEAD, x - NRD);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    commit_scales();
+  };
+  // the last K steps: waits, refills (possibly low-rank steps) and reads
+  // under branches, then the half-1 MFMAs
+  auto kstep_tail = [&](int r) {
+    phase_a(r);
+    if (r + 1 < total) {
+      // steps after r + 1 already requested: r + 2 .. r + STAGES - 1, those that exist
+      if (C::STAGES > 3 && r + 3 < total) SVDQ_WAIT_VM(2 * LPW);
+      else if (r + 2 < total) SVDQ_WAIT_VM(LPW);
+      else SVDQ_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+    }
+    if (r + AHEAD < total) {
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) issue_any(r + AHEAD, k);
+    }
+    if (r + 1 < nk) {
+#pragma unroll
+      for (int x = 0; x < NRD; ++x) rd_next((r + 1) % C::STAGES, x);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < TI * TJ; ++k) mfma_hij(1, k / TJ, k % TJ);
+    __builtin_amdgcn_sched_barrier(0);
+    commit_scales();
+  };
+  int r = 0;
+  for (; r + AHEAD < nk; ++r) kstep(r);
+  for (; r < nk; ++r) kstep_tail(r);
+
+  // ---- low-rank steps: T L2 on the 32 x 32 x 16 16-bit MFMA (the stage of
+  // step q was waited for by the previous barrier)
+  for (int q = nk; q < total; ++q) {
+    SVDQ_WAIT_LGKM0();
+    if (q > nk) {
+      SVDQ_WAIT_VM(0);
+      __builtin_amdgcn_s_barrier();
+    }
+    const int st = q % C::STAGES;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) fa[h][i] = rd_a(st, h, i);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) fb[h][j] = rd_b(st, h, j);
+    }
+    SVDQ_WAIT_LGKM0();
+    if (q + AHEAD < total) {
+      __builtin_amdgcn_s_barrier();      // every wave has read stage q before it is refilled
+#pragma unroll
+      for (int k = 0; k < LPW; ++k) issue_any(q + AHEAD, k);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (2 * (q - nk) + h < p.nchunks16) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) acc[i][j] = mfma32x16<DT>(fa[h][i], fb[h][j], acc[i][j]);
+      }
+  }
+  SVDQ_WAIT_LGKM0();
+  SVDQ_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();          // every wave is done with the ring
+
+  // ---- epilogue: (GELU,) round; stage the workgroup tile in LDS as
+  // [token][column] rows, then store whole row segments
+#pragma unroll
+  for (int i = 0; i < TI; ++i) {
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      // accumulator 4gg + x of tile (i, j): column 32i + 8gg + 4(lane / 32) + x, token 32j + lane % 32
+      const int nl = 32 * (ia0 + i) + 8 * gg + 4 * (lane >> 5);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        float vv[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          vv[x] = acc[i][j][4 * gg + x];
+          if constexpr (GELU) vv[x] = gelu_erf(vv[x]);
+        }
+        const int ml = 32 * (jb0 + j) + (lane & 31);
+        *reinterpret_cast<u32x2*>(smem + ml * C::PITCH + nl * 2) = u32x2{pack2<DT>(vv[0], vv[1]), pack2<DT>(vv[2], vv[3])};
+      }
+    }
+  }
+  SVDQ_WAIT_LGKM0();
+  __builtin_amdgcn_s_barrier();
+  // 16-byte pieces of the staged rows: piece c of row t covers columns 8c .. 8c + 7
+  constexpr int PPR = C::TN / 8;                       // pieces per row
+  constexpr int NPC = C::TM * PPR;                     // pieces in the tile
+  const int tid = wave * 64 + lane;
+#pragma unroll 2
+  for (int pc = tid; pc < NPC; pc += 64 * C::NW) {
+    const int row = pc / PPR, c = pc % PPR;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(smem + row * C::PITCH + c * 16);
+    if (m0 + row < p.M && n0 + 8 * c < p.N)
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + 8 * c));
+  }
+}
+
+template <int DT, bool GELU, class C>
+__global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // XCD-aware grouped tile order (as in k2_mx)
+  const int T = p.tiles_n * p.tiles_m;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, kx = bid >> 3, per = T >> 3, rem = T & 7;
+  const int tile = xcd * per + (xcd < rem ? xcd : rem) + kx;
+  const int gsz_full = mx::GROUP_M * p.tiles_n;
+  const int grp = tile / gsz_full, first_m = grp * mx::GROUP_M;
+  const int gm = (p.tiles_m - first_m) < mx::GROUP_M ? (p.tiles_m - first_m) : mx::GROUP_M;
+  const int within = tile - grp * gsz_full;
+  const int tm = first_m + within % gm, tn = within / gm;
+  const int64_t n0 = int64_t(tn) * C::TN, m0 = int64_t(tm) * C::TM;
+  const int pa = ((wave % C::WN) * C::TI) & 1, pb = ((wave / C::WN) * C::TJ) & 1;
+  // one load class (every wave issues the same stage loads), four tile parities
+  static_assert(C::FR == 0, "one load class");
+  if (pb == 0) {
+    if (pa == 0) mx8_tile<DT, GELU, C, 0, 0, 1>(p, smem, wave, lane, n0, m0);
+    else mx8_tile<DT, GELU, C, 1, 0, 1>(p, smem, wave, lane, n0, m0);
+  } else {
+    if (pa == 0) mx8_tile<DT, GELU, C, 0, 1, 1>(p, smem, wave, lane, n0, m0);
+    else mx8_tile<DT, GELU, C, 1, 1, 1>(p, smem, wave, lane, n0, m0);
+  }
+}
+
 // ------------------------------------------- unfused low-rank up-projection
 // The unfused low-rank baseline's last pass: Y = round16(GELU?(Y + T L2)),
 // reading and rewriting the 4-bit GEMM's rounded output.  Same fragment
@@ -1643,6 +2056,7 @@ MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   mp.nchunks16 = kp.nchunks16;
   mp.tiles_n = int(svdq::ceil_div(kp.N, 256));
   mp.tiles_m = int(w.Mp / 256);
+  mp.tiles_m_pad32 = int(w.Mp / 32);
   mp.off_wq = int(kp.wq - reinterpret_cast<const uint8_t*>(kp.l2));
   mp.off_sw = int(kp.sw - reinterpret_cast<const uint8_t*>(kp.l2));
   mp.off_sx = int(kp.sx - kp.xq);
@@ -1656,6 +2070,30 @@ void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipSt
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
   if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
   else hipLaunchKernelGGL((k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
+}
+
+template <int DT, class C>
+void launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+  MxParams mp = mx_params(kp, w);
+  mp.tiles_n = int(svdq::ceil_div(kp.N, C::TN));
+  mp.tiles_m = int(svdq::ceil_div(w.Mp, C::TM));
+  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  if (gelu) hipLaunchKernelGGL((k2_mx8<DT, true, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+  else hipLaunchKernelGGL((k2_mx8<DT, false, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+}
+
+// MXFP4 GEMM.  Without GELU: k2_mx (256 x 256 tiles, four waves, one per
+// SIMD).  With GELU: k2_mx8 with 192 x 192 tiles two to a compute unit, so
+// one workgroup's GELU epilogue (VALU work after the K loop) runs under the
+// other's MFMAs.  Measured on the FLUX fc1 shape, same process, interleaved
+// rounds: without GELU the two kernels and an eight-wave 384 x 192 variant
+// (three whole rounds) are within 3% of one another -- the clock falls to
+// the power limit either way -- while with GELU the paired tiles take 134 us
+// against 145 us.
+template <int DT>
+void launch_k2_mx4(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+  if (gelu) launch_k2_mx8<DT, mx8::Pair>(kp, w, true, st);
+  else launch_k2_mx<DT>(kp, w, false, st);
 }
 
 template <int DT>
@@ -1759,8 +2197,8 @@ void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
     if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
     else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
   } else {
-    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16>(kp, w, gelu, stream);
-    else launch_k2_mx<SVDQ_F16>(kp, w, gelu, stream);
+    if (L->dtype == SVDQ_BF16) launch_k2_mx4<SVDQ_BF16>(kp, w, gelu, stream);
+    else launch_k2_mx4<SVDQ_F16>(kp, w, gelu, stream);
   }
 }
 

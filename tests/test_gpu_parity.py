@@ -88,6 +88,18 @@ def test_branch_wider_than_64(fmt, K):
     G.run_layer_case(d, fmt, 64, lora=True)
 
 
+@pytest.mark.parametrize("K", [128, 384, 640, 1536])
+@pytest.mark.parametrize("dtype", [o.BF16, o.F16])
+def test_gelu_gemm_paired_tiles(K, dtype):
+    # the MXFP4 GEMM with a GELU epilogue (192 x 192 tiles, two workgroups
+    # per compute unit): fewer K steps than stages (K = 128, 384), the
+    # steady-state loop (K = 640, 1536), a 96-wide branch (three low-rank
+    # steps, some requested by the last K steps), ragged tokens and a partial
+    # last column tile (640 = 3 x 192 + 64), every output checked
+    d = _small(500, K, 640, dtype, o.MXFP4, 64, lora=32, seed=90 + K)
+    G.run_layer_case(d, o.MXFP4, 64, lora=True, gelu=True, alpha=0.75)
+
+
 @pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
 def test_refined_pack_forward(fmt):
     # a pack whose low-rank split was refined (device blob written through
