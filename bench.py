@@ -60,6 +60,11 @@ def parse():
     ap.add_argument("--chain-study", action="store_true",
                     help="instead of the headline line, time the FLUX MLP pair (fc1 + GELU -> fc2, MXFP4) with "
                          "fc2's activation pass as its own kernel and chained into fc1's GEMM epilogue")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline line, print one JSON record per (config, shape, format) over "
+                         "every shape of the five workload configs: forward, activation-kernel and GEMM times "
+                         "and their rooflines")
+    ap.add_argument("--sweep-configs", default="1,2,3,4,5", help="configs the sweep covers")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the layer, time a plain device copy of MIB MiB (the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters)")
@@ -321,6 +326,117 @@ def chain_study(args):
         "runs_us": {k: [round(x, 2) for x in v] for k, v in runs.items()}}), flush=True)
 
 
+def sweep(args):
+    """Every shape of the five workload configs, each format it names: the
+    forward (activation kernel + GEMM, HIP events around each kernel, 20
+    steps over 2 rotating buffer sets after 5 warm-up steps), as TOPS and
+    against its roofline max(ops / MFMA peak, bytes / HBM peak)."""
+    import ctypes as C
+    import torch
+    from diffusion_smooth_group_amd import svdq as S
+    from diffusion_smooth_group_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = S.lib_handle()
+    stream = torch.cuda.current_stream()
+    sh = C.c_void_p(stream.cuda_stream)
+    fmt_codes = {wl.MXFP4: S.FMT_MXFP4_G32, wl.INT4: S.FMT_INT4_G64}
+    steps, warm, nrot = 20, 5, 2
+    cfgs = [int(c) for c in args.sweep_configs.split(",")]
+    fc1_cache = {}     # the MLP pair's first layer, whose output feeds the second
+    n_rec = 0
+    for cfg in cfgs:
+        for spec in wl.config_shapes(cfg):
+            dt = S.BF16 if spec.dtype == wl.BF16 else S.F16
+            t_gen = time.time()
+            if spec.x_dist == "gelu_of_fc1":
+                key = (spec.seed[0], spec.seed[1] - 1)
+                d = wl.generate(spec, fc1_inputs=fc1_cache.get(key))
+            else:
+                d = wl.generate(spec)
+                if cfg == 3 and "fc1" in spec.name:
+                    fc1_cache[tuple(spec.seed)] = d
+            t_gen = time.time() - t_gen
+            # MLP fc1 layers carry the block's GELU in their epilogue
+            gelu = "fc1" in spec.name
+            M, K, N = spec.M, spec.K, spec.N
+            Xd = S.bits_to_device(d["X"], dt, dev)
+            am = S.activation_absmax(Xd, dt)
+            torch.cuda.synchronize()
+            for fmt in spec.formats:
+                fmt_name = fmt
+                rank, rl = spec.rank, spec.lora_rank
+                t_pack = time.time()
+                lin = S.SVDQLinear.pack(d["W"], dt, am.cpu().numpy(), rank, fmt_codes[fmt], d["bias"],
+                                        rank_capacity=rank + rl)
+                if rl:
+                    lin.attach_lora(d["lora_A"], d["lora_B"], 1.0)
+                t_pack = time.time() - t_pack
+                ra = rank + rl
+                layers, blobs = [lin.layer], [lin.blob]
+                for _ in range(nrot - 1):
+                    b = torch.empty_like(lin.blob)
+                    layers.append(S.layer_copy(lin.layer, S._t_ptr(b), b.numel(), True))
+                    blobs.append(b)
+                Xs = [Xd] + [Xd.clone() for _ in range(nrot - 1)]
+                Ys = [torch.empty((M, N), dtype=Xd.dtype, device=dev) for _ in range(nrot)]
+                wsb = S.workspace_size(lin.layer, M)
+                wss = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nrot)]
+                flags = S.FLAG_GELU if gelu else 0
+
+                def step(i, ev=None):
+                    j = i % nrot
+                    if ev is not None:
+                        ev[0].record(stream)
+                    rc = lib.svdq_quantize_activations(C.byref(layers[j]), S._t_ptr(Xs[j]), M, K, S._t_ptr(wss[j]),
+                                                       wsb, sh)
+                    if rc != 0:
+                        raise S.SvdqError("svdq_quantize_activations", rc)
+                    if ev is not None:
+                        ev[1].record(stream)
+                    rc = lib.svdq_gemm_forward(C.byref(layers[j]), M, S._t_ptr(Ys[j]), N, S._t_ptr(wss[j]), wsb,
+                                               flags, sh)
+                    if rc != 0:
+                        raise S.SvdqError("svdq_gemm_forward", rc)
+                    if ev is not None:
+                        ev[2].record(stream)
+                for i in range(warm):
+                    step(i)
+                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+                torch.cuda.synchronize()
+                for i in range(steps):
+                    step(i, evs[i])
+                torch.cuda.synchronize()
+                t1 = float(np.median([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
+                t2 = float(np.median([e[1].elapsed_time(e[2]) for e in evs]) * 1e3)
+                tf = float(np.median([e[0].elapsed_time(e[2]) for e in evs]) * 1e3)
+                ops = 2.0 * M * K * N
+                peak = PEAK_TFLOPS[fmt_name]
+                b2 = k2_bytes(M, K, N, ra, fmt_name)
+                b1 = k1_bytes(M, K, ra, fmt_name)
+                t_mfma = ops / (peak * 1e12) * 1e6
+                t_hbm = b2 / (HBM_PEAK_GBS * 1e9) * 1e6
+                floor = max(t_mfma, t_hbm)
+                rec = {"sweep": True, "config": cfg, "shape": spec.name, "M": M, "K": K, "N": N,
+                       "format": fmt_name, "dtype": spec.dtype, "rank_active": ra, "gelu": gelu,
+                       "t_fwd_us": round(tf, 2), "t_k1_us": round(t1, 2), "t_gemm_us": round(t2, 2),
+                       "tops_fwd": round(ops / (tf * 1e-6) / 1e12, 1), "tops_gemm": round(ops / (t2 * 1e-6) / 1e12, 1),
+                       "gemm_roofline": {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "peak_tflops": peak,
+                                         "t_mfma_us": round(t_mfma, 2), "t_hbm_us": round(t_hbm, 2),
+                                         "algorithmic_bytes": b2, "frac": round(floor / t2, 4)},
+                       "k1_roofline": {"bound": "hbm", "algorithmic_bytes": b1,
+                                       "frac": round(b1 / (HBM_PEAK_GBS * 1e9) * 1e6 / t1, 4)},
+                       "pack_s": round(t_pack, 2), "gen_s": round(t_gen, 2)}
+                if fmt_name == "int4_g64":
+                    rec["gemm_roofline"]["frac_vs_fp4_peak"] = round(ops / (PEAK_TFLOPS["mxfp4_g32"] * 1e12) * 1e6 / t2, 4)
+                print(json.dumps(rec), flush=True)
+                n_rec += 1
+                del layers, blobs, Xs, Ys, wss, lin
+                torch.cuda.empty_cache()
+            del Xd, d
+    print(json.dumps({"sweep_done": True, "records": n_rec, "configs": cfgs}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,6 +451,9 @@ def main():
         return
     if args.chain_study:
         chain_study(args)
+        return
+    if args.sweep:
+        sweep(args)
         return
     import torch
     from diffusion_smooth_group_amd import svdq as S
@@ -399,6 +518,7 @@ def main():
         if rc != 0:
             raise S.SvdqError("svdq_gemm_forward", rc)
 
+    sclk_idle = S.probe_clock(stream)
     for i in range(args.warmup):
         fwd(i)
     torch.cuda.synchronize()
@@ -414,36 +534,67 @@ def main():
     wall = time.perf_counter() - tw0
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- per-kernel launch durations (HIP events on the launch stream): the
-    # mean over n back-to-back launches between two events, and the spread of
-    # n launches each bracketed by its own pair of events
-    def per_launch(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        mean = e0.elapsed_time(e1) * 1e3 / n
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i in range(n):
-            evs[i][0].record(stream)
-            fn(i)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        ts = np.array([a.elapsed_time(b) for a, b in evs]) * 1e3   # us
-        return float(mean), float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90))
-
-    for i in range(nrot):       # workspaces hold this step's activations for k2-only timing
+    # ---- the same forward loop again (after the timed region), each step as
+    # its two kernels -- svdq_quantize_activations and svdq_gemm_forward, the
+    # launches svdq_linear_forward makes -- with HIP events on the launch
+    # stream before, between and after them: per-kernel durations inside
+    # forwards, K1 + K2 = the forward by construction
+    n_inst = max(args.steps, args.kernel_iters)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_inst)]
+    for i in range(n_inst):
+        evs[i][0].record(stream)
         k1(i)
+        evs[i][1].record(stream)
+        k2(i)
+        evs[i][2].record(stream)
     torch.cuda.synchronize()
-    k1_stats = per_launch(k1, args.kernel_iters)
-    k2_stats = per_launch(k2, args.kernel_iters)
+    sclk_after = S.probe_clock(stream)      # a light kernel right after the loop
+    # three more forwards with the GEMM traced (per-workgroup wall and
+    # shader-clock counters): the clock the GEMM itself ran at
+    traces = []
+    for i in range(3):
+        # the traced launch sits inside a run of forwards (no idle gap before it)
+        for q in range(10):
+            fwd(q)
+        j = (n_inst + i) % nrot
+        k1(n_inst + i)
+        rc = lib.svdq_gemm_forward(C.byref(layers[j]), M, S._t_ptr(Ys[j]), N, S._t_ptr(wss[j]), ws_bytes,
+                                   S.FLAG_TRACE, sh)
+        if rc != 0:
+            raise S.SvdqError("svdq_gemm_forward", rc)
+        for q in range(3):
+            fwd(q)
+        rec, hz = S.trace_read()
+        r = rec.astype(np.float64)
+        wg_ticks = r[:, 2] - r[:, 0]
+        traces.append({"sclk_mhz": float((r[:, 3] - r[:, 1]).sum() / wg_ticks.sum() * hz * 1e-6),
+                       "span_us": float((r[:, 2].max() - r[:, 0].min()) / hz * 1e6),
+                       "wg_us": np.percentile(wg_ticks / hz * 1e6, [10, 50, 90]).tolist(),
+                       "workgroups": int(len(r))})
+    tr = sorted(traces, key=lambda t: t["span_us"])[1]          # the median of the three by span
+    t_k1 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
+    t_k2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
+    t_fw = t_k1 + t_k2
+
+    def stats(t):
+        return {"mean": round(float(np.mean(t)), 2), "median": round(float(np.median(t)), 2),
+                "p10": round(float(np.percentile(t, 10)), 2), "p90": round(float(np.percentile(t, 90)), 2)}
+
+    # the matrix core's sustained FP4 rate with no memory traffic, on random
+    # and on zero operands (second of two runs each)
+    ceil = {}
+    for rnd, key in ((True, "random"), (False, "zero")):
+        S.probe_mfma_rate(rnd, 2000, stream)
+        tf, mhz = S.probe_mfma_rate(rnd, 2000, stream)
+        ceil[key + "_tflops"] = round(tf, 1)
+        ceil[key + "_mhz"] = round(mhz, 1)
 
     flops = 2.0 * M * K * N
     tops = flops / (ms_step * 1e-3) / 1e12
-    k2_tflops = flops / (k2_stats[0] * 1e-6) / 1e12
-    k1_gbs = k1_bytes(M, K, args.rank, fmt_name) / (k1_stats[0] * 1e-6) / 1e9
+    k2_mean = float(np.mean(t_k2))
+    k1_mean = float(np.mean(t_k1))
+    k2_tflops = flops / (k2_mean * 1e-6) / 1e12
+    k1_gbs = k1_bytes(M, K, args.rank, fmt_name) / (k1_mean * 1e-6) / 1e9
     peak = PEAK_TFLOPS[fmt_name]
     out = {
         "metric": METRIC if args.fmt != "int8" else METRIC.replace("W4A4", "W8A8"),
@@ -466,14 +617,23 @@ def main():
                      "unit": "TFLOP/s", "frac": round(k2_tflops / peak, 4),
                      "traffic": measured_traffic(f"flux_{args.workload}_{M}x{K}x{N}", fmt_name),
                      "algorithmic_flops_per_launch": flops,
-                     "algorithmic_bytes_per_launch": k2_bytes(M, K, N, args.rank, fmt_name)},
+                     "algorithmic_bytes_per_launch": k2_bytes(M, K, N, args.rank, fmt_name),
+                     "time_source": "mean K2 duration inside the forward loop (HIP events around each kernel)",
+                     "frac_of_sustained_fp4_rate": round(k2_tflops / ceil["random_tflops"], 4)
+                     if fmt_name == "mxfp4_g32" else None,
+                     "frac_at_traced_clock": round(k2_tflops / (peak * tr["sclk_mhz"] / 2400.0), 4)},
         "k1_roofline": {"bound": "hbm", "kernel": "k1_act", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                         "algorithmic_bytes_per_launch": k1_bytes(M, K, args.rank, fmt_name)},
-        "kernel_us": {"k1_act": {"mean": round(k1_stats[0], 2), "median": round(k1_stats[1], 2),
-                                 "p10": round(k1_stats[2], 2), "p90": round(k1_stats[3], 2)},
-                      "k2_gemm": {"mean": round(k2_stats[0], 2), "median": round(k2_stats[1], 2),
-                                  "p10": round(k2_stats[2], 2), "p90": round(k2_stats[3], 2)}},
+        "kernel_us": {"k1_act": stats(t_k1), "k2_gemm": stats(t_k2), "forward": stats(t_fw),
+                      "launches": n_inst},
+        "sclk_mhz": {"idle_probe": round(sclk_idle, 1), "probe_after_forward_loop": round(sclk_after, 1),
+                     "gemm_traced": round(tr["sclk_mhz"], 1)},
+        "k2_trace": {"workgroups": tr["workgroups"], "span_us": round(tr["span_us"], 2),
+                     "workgroup_us_p10_p50_p90": [round(x, 2) for x in tr["wg_us"]],
+                     "note": "median (by span) of three traced GEMM launches, each inside a run of forwards; "
+                             "sclk = shader cycles / wall time summed over workgroups"},
+        "mfma_fp4_sustained": ceil,
         "gemm_only_tops": round(k2_tflops, 2),
         "timed_wall_s": round(wall, 4),
         "pack_s": round(t_pack, 2),

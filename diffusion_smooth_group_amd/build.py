@@ -42,9 +42,10 @@ def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     cxx = shutil.which("g++") or "g++"
     objs = []
-    k_obj = os.path.join(BUILD, "svdq_kernels.o")
-    _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, "svdq_kernels.hip"), "-o", k_obj])
-    objs.append(k_obj)
+    for name in ("svdq_kernels", "svdq_probe"):
+        obj = os.path.join(BUILD, name + ".o")
+        _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, name + ".hip"), "-o", obj])
+        objs.append(obj)
     p_obj = os.path.join(BUILD, "svdq_pack.o")
     _run([cxx] + HOST_FLAGS + ["-ffp-contract=off", "-c", os.path.join(CSRC, "svdq_pack.cpp"), "-o", p_obj])
     objs.append(p_obj)

@@ -473,6 +473,7 @@ struct K2Params {
   uint16_t* Y;
   int64_t ldy, M, N, K;
   int slots, nchunks, nchunks16;
+  unsigned long long* trace;   // GEMM trace records (SVDQ_FLAG_TRACE) or null
 };
 
 __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
@@ -480,6 +481,21 @@ __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
   // both operands use the same order, so the dot product is unchanged)
   return i32x4{int((d0 << 4) & 0xF0F0F0F0u), int((d1 << 4) & 0xF0F0F0F0u), int(d0 & 0xF0F0F0F0u),
                int(d1 & 0xF0F0F0F0u)};
+}
+
+// GEMM tracing (SVDQ_FLAG_TRACE): thread 0 of each workgroup writes the
+// wall-clock counter and the shader-clock counter at the workgroup's start
+// (records 0, 1) and, after a workgroup barrier, once every wave has issued
+// its last store (records 2, 3).
+constexpr int kTraceMax = 65536;       // workgroups a trace holds
+__device__ __forceinline__ void trace_mark(unsigned long long* trace, int at) {
+  const unsigned wg = blockIdx.x + gridDim.x * blockIdx.y;   // linear workgroup index (1-D and 2-D grids)
+  if (at != 0 && trace != nullptr) __syncthreads();          // uniform: the whole workgroup takes it or none
+  if (trace != nullptr && threadIdx.x == 0 && wg < unsigned(kTraceMax)) {
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime(), ck = __builtin_amdgcn_s_memtime();
+    trace[4 * size_t(wg) + at] = rt;
+    trace[4 * size_t(wg) + at + 1] = ck;
+  }
 }
 
 // GELU in its exact form x Phi(x), written without branches so an epilogue
@@ -526,6 +542,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
 // VALU), each step loaded one step ahead, and several waves share a SIMD.
 template <int DT, bool GELU>
 __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
+  trace_mark(p.trace, 0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const bool k0 = lane < 16;             // lanes that carry k = 0..3 of a 16 x 16 x 16 operand
@@ -664,6 +681,7 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
     const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OP + col * 2);
     if (m0 + row < p.M) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col));
   }
+  trace_mark(p.trace, 2);
 }
 
 
@@ -884,6 +902,7 @@ struct MxParams {
   // and of the token-side regions from xq (all in the workspace); both spans
   // are below 2 GiB, so the stage loads take them as scalar offsets
   int off_wq, off_sw, off_sx, off_t;
+  unsigned long long* trace;   // GEMM trace records (SVDQ_FLAG_TRACE) or null
   // Epilogue chaining (CHAIN): this layer's output is the next layer's
   // input.  nx_invlam: the next layer's 1/lambda over this layer's N
   // columns; nx_l1x: its L1x in the activation kernel's tiling; nx_xq,
@@ -1038,6 +1057,7 @@ __device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t*
 
 template <int DT, bool GELU, bool CHAIN = false, bool I8 = false>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
+  trace_mark(p.trace, 0);
   // one LDS object (a second one makes the compiler wait for every global->LDS
   // load before any LDS read)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
@@ -1399,6 +1419,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     }
     if constexpr (CHAIN) chain_epilogue<DT>(p, smem, ob, wave, lane, m0, n0, nw, mw);
   }
+  trace_mark(p.trace, 2);
 }
 
 // ---------------------------------------- k2_mx8 (MXFP4, two waves per SIMD)
@@ -1788,6 +1809,7 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
 
 template <int DT, bool GELU, class C>
 __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
+  trace_mark(p.trace, 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // XCD-aware grouped tile order (as in k2_mx)
@@ -1811,6 +1833,7 @@ __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
     if (pa == 0) mx8_tile<DT, GELU, C, 0, 1, 1>(p, smem, wave, lane, n0, m0);
     else mx8_tile<DT, GELU, C, 1, 1, 1>(p, smem, wave, lane, n0, m0);
   }
+  trace_mark(p.trace, 2);
 }
 
 // ------------------------------------------- unfused low-rank up-projection
@@ -2042,11 +2065,13 @@ void launch_k1_w8(const K1Params& kp, int64_t Mp, hipStream_t st) {
   else hipLaunchKernelGGL((k1_w8<DT, MAXJT>), grid, block, 0, st, kp);
 }
 
+// (the GEMM launchers return the number of workgroups they launch)
 template <int DT>
-void launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
+unsigned launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
   if (gelu) hipLaunchKernelGGL((k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
   else hipLaunchKernelGGL((k2_int4<DT, false>), grid, dim3(256), 0, st, kp);
+  return grid.x * grid.y;
 }
 
 MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
@@ -2061,25 +2086,28 @@ MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   mp.off_sw = int(kp.sw - reinterpret_cast<const uint8_t*>(kp.l2));
   mp.off_sx = int(kp.sx - kp.xq);
   mp.off_t = int(reinterpret_cast<const uint8_t*>(kp.t) - kp.xq);
+  mp.trace = kp.trace;
   return mp;
 }
 
 template <int DT, bool I8 = false>
-void launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+unsigned launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   const MxParams mp = mx_params(kp, w);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
   if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
   else hipLaunchKernelGGL((k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
+  return T;
 }
 
 template <int DT, class C>
-void launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+unsigned launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   MxParams mp = mx_params(kp, w);
   mp.tiles_n = int(svdq::ceil_div(kp.N, C::TN));
   mp.tiles_m = int(svdq::ceil_div(w.Mp, C::TM));
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
   if (gelu) hipLaunchKernelGGL((k2_mx8<DT, true, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
   else hipLaunchKernelGGL((k2_mx8<DT, false, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+  return T;
 }
 
 // MXFP4 GEMM.  Without GELU: k2_mx (256 x 256 tiles, four waves, one per
@@ -2091,9 +2119,9 @@ void launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipS
 // the power limit either way -- while with GELU the paired tiles take 134 us
 // against 145 us.
 template <int DT>
-void launch_k2_mx4(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
-  if (gelu) launch_k2_mx8<DT, mx8::Pair>(kp, w, true, st);
-  else launch_k2_mx<DT>(kp, w, false, st);
+unsigned launch_k2_mx4(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
+  if (gelu) return launch_k2_mx8<DT, mx8::Pair>(kp, w, true, st);
+  return launch_k2_mx<DT>(kp, w, false, st);
 }
 
 template <int DT>
@@ -2121,7 +2149,40 @@ svdq_status check_device_layer(const svdq_layer* L) {
 
 }  // namespace
 
+// ------------------------------------------------------------- GEMM tracing
+// Library-owned trace of the last traced GEMM launch on each device (4
+// counters per workgroup, see trace_mark); its device address is looked up
+// once per device.
+static __device__ unsigned long long trace_buf[kTraceMax * 4];
+
 namespace {
+
+struct TraceState {
+  std::mutex mu;
+  unsigned long long* ptr[64] = {};
+  unsigned n[64] = {};       // workgroups of the last traced launch
+};
+TraceState g_trace;
+
+svdq_status trace_ptr(unsigned long long** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SVDQ_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_trace.mu);
+  if (g_trace.ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(trace_buf)) != hipSuccess || p == nullptr) return SVDQ_ERR_HIP;
+    g_trace.ptr[dev] = static_cast<unsigned long long*>(p);
+  }
+  *out = g_trace.ptr[dev];
+  return SVDQ_OK;
+}
+
+void trace_set_count(unsigned n) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return;
+  std::lock_guard<std::mutex> lock(g_trace.mu);
+  g_trace.n[dev] = n < unsigned(kTraceMax) ? n : unsigned(kTraceMax);
+}
 
 enum K1Mode { K1_BOTH, K1_QUANT, K1_PROJ };
 
@@ -2183,23 +2244,28 @@ K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, con
   const int ra = lowrank ? L->rank_active : 0;
   kp.nchunks = int(svdq::ceil_div(ra, 32));
   kp.nchunks16 = int(svdq::ceil_div(ra, 16));
+  kp.trace = nullptr;
   return kp;
 }
 
-// K2 on checked arguments; lowrank = false leaves the low-rank branch out
+// K2 on checked arguments; lowrank = false leaves the low-rank branch out;
+// trace: device trace records or null
 void run_k2(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint8_t* ws, const svdq::WsOffsets& w,
-            bool gelu, bool lowrank, hipStream_t stream) {
-  const K2Params kp = k2_params(L, M, Y_dev, ldy, ws, w, lowrank);
+            bool gelu, bool lowrank, hipStream_t stream, unsigned long long* trace = nullptr) {
+  K2Params kp = k2_params(L, M, Y_dev, ldy, ws, w, lowrank);
+  kp.trace = trace;
+  unsigned nwg = 0;
   if (L->fmt == SVDQ_FMT_INT8_W8A8) {
-    if (L->dtype == SVDQ_BF16) launch_k2_mx<SVDQ_BF16, true>(kp, w, gelu, stream);
-    else launch_k2_mx<SVDQ_F16, true>(kp, w, gelu, stream);
+    if (L->dtype == SVDQ_BF16) nwg = launch_k2_mx<SVDQ_BF16, true>(kp, w, gelu, stream);
+    else nwg = launch_k2_mx<SVDQ_F16, true>(kp, w, gelu, stream);
   } else if (L->fmt == SVDQ_FMT_INT4_G64) {
-    if (L->dtype == SVDQ_BF16) launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
-    else launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
+    if (L->dtype == SVDQ_BF16) nwg = launch_k2_int4<SVDQ_BF16>(kp, w.Mp, gelu, stream);
+    else nwg = launch_k2_int4<SVDQ_F16>(kp, w.Mp, gelu, stream);
   } else {
-    if (L->dtype == SVDQ_BF16) launch_k2_mx4<SVDQ_BF16>(kp, w, gelu, stream);
-    else launch_k2_mx4<SVDQ_F16>(kp, w, gelu, stream);
+    if (L->dtype == SVDQ_BF16) nwg = launch_k2_mx4<SVDQ_BF16>(kp, w, gelu, stream);
+    else nwg = launch_k2_mx4<SVDQ_F16>(kp, w, gelu, stream);
   }
+  if (trace != nullptr) trace_set_count(nwg);
 }
 
 // the MXFP4 GEMM addresses the blob from L2 and the workspace from the
@@ -2234,7 +2300,8 @@ void run_up(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, const uint
   }
 }
 
-constexpr unsigned SVDQ_FLAGS_ALL = unsigned(SVDQ_FLAG_GELU) | unsigned(SVDQ_FLAG_UNFUSED_LOWRANK);
+constexpr unsigned SVDQ_FLAGS_ALL =
+    unsigned(SVDQ_FLAG_GELU) | unsigned(SVDQ_FLAG_UNFUSED_LOWRANK) | unsigned(SVDQ_FLAG_TRACE);
 
 svdq_status check_x(const svdq_layer* L, const void* X_dev, int64_t ldx) {
   if (!X_dev) return SVDQ_ERR_INVALID_ARG;
@@ -2347,12 +2414,14 @@ extern "C" svdq_status svdq_gemm_forward(const svdq_layer* L, int64_t M, void* Y
                                          const void* ws_dev, size_t ws_bytes, unsigned flags, hipStream_t stream) {
   svdq_status st = check_device_layer(L);
   if (st != SVDQ_OK) return st;
-  if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU)) != 0u) return SVDQ_ERR_INVALID_ARG;
+  if (M < 0 || (flags & ~unsigned(SVDQ_FLAG_GELU | SVDQ_FLAG_TRACE)) != 0u) return SVDQ_ERR_INVALID_ARG;
   if (M == 0) return SVDQ_OK;
   svdq::WsOffsets w;
   if ((st = check_y(L, Y_dev, ldy)) != SVDQ_OK || (st = check_ws(L, M, ws_dev, ws_bytes, &w)) != SVDQ_OK) return st;
   if (!mx_offsets_fit(L, w)) return SVDQ_ERR_UNSUPPORTED;
-  run_k2(L, M, Y_dev, ldy, static_cast<const uint8_t*>(ws_dev), w, (flags & SVDQ_FLAG_GELU) != 0u, true, stream);
+  unsigned long long* trace = nullptr;
+  if ((flags & SVDQ_FLAG_TRACE) != 0u && (st = trace_ptr(&trace)) != SVDQ_OK) return st;
+  run_k2(L, M, Y_dev, ldy, static_cast<const uint8_t*>(ws_dev), w, (flags & SVDQ_FLAG_GELU) != 0u, true, stream, trace);
   return launch_ok();
 }
 
@@ -2371,15 +2440,17 @@ extern "C" svdq_status svdq_linear_forward(const svdq_layer* L, const void* X_de
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
   if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) != 0u && L->fmt == SVDQ_FMT_INT8_W8A8) return SVDQ_ERR_UNSUPPORTED;
+  unsigned long long* trace = nullptr;
+  if ((flags & SVDQ_FLAG_TRACE) != 0u && (st = trace_ptr(&trace)) != SVDQ_OK) return st;
   if ((flags & SVDQ_FLAG_UNFUSED_LOWRANK) == 0u || L->rank_active == 0) {
     run_k1(L, X_dev, M, ldx, ws, w, K1_BOTH, stream);
-    run_k2(L, M, Y_dev, ldy, ws, w, gelu, true, stream);
+    run_k2(L, M, Y_dev, ldy, ws, w, gelu, true, stream, trace);
   } else {
     // the low-rank branch as separate passes: quantize, down-project (a
     // second read of X), 4-bit GEMM + bias, then Y += T L2 (+ GELU)
     run_k1(L, X_dev, M, ldx, ws, w, K1_QUANT, stream);
     run_k1(L, X_dev, M, ldx, ws, w, K1_PROJ, stream);
-    run_k2(L, M, Y_dev, ldy, ws, w, false, false, stream);
+    run_k2(L, M, Y_dev, ldy, ws, w, false, false, stream, trace);
     run_up(L, M, Y_dev, ldy, ws, w, gelu, stream);
   }
   return launch_ok();
@@ -2424,6 +2495,30 @@ extern "C" svdq_status svdq_linear_forward_noalloc(const svdq_layer* L, const vo
   void* ws = nullptr;
   if ((st = scratch_for_current_device(&ws)) != SVDQ_OK) return st;
   return svdq_linear_forward(L, X_dev, M, ldx, Y_dev, ldy, ws, size_t(SVDQ_NOALLOC_SCRATCH_BYTES), flags, stream);
+}
+
+extern "C" svdq_status svdq_trace_read(unsigned long long* records, int max_records, int* n_records,
+                                       double* wall_hz) {
+  if (!n_records || !wall_hz || max_records < 0 || (max_records > 0 && !records)) return SVDQ_ERR_INVALID_ARG;
+  int dev = -1, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SVDQ_ERR_HIP;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) return SVDQ_ERR_HIP;
+  unsigned long long* ptr = nullptr;
+  svdq_status st = trace_ptr(&ptr);
+  if (st != SVDQ_OK) return st;
+  unsigned n = 0;
+  {
+    std::lock_guard<std::mutex> lock(g_trace.mu);
+    n = g_trace.n[dev];
+  }
+  *n_records = int(n);
+  *wall_hz = double(khz) * 1e3;
+  const unsigned k = n < unsigned(max_records) ? n : unsigned(max_records);
+  if (k == 0) return SVDQ_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return SVDQ_ERR_HIP;
+  if (hipMemcpy(records, ptr, size_t(k) * 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost) != hipSuccess)
+    return SVDQ_ERR_HIP;
+  return SVDQ_OK;
 }
 
 extern "C" svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int64_t ldx,

@@ -24,6 +24,7 @@ F16 = 0
 BF16 = 1
 FLAG_GELU = 1
 FLAG_UNFUSED_LOWRANK = 2
+FLAG_TRACE = 4
 MAX_RANK_CAPACITY = 128
 
 FMT_CODES = {"int4_g64": FMT_INT4_G64, "mxfp4_g32": FMT_MXFP4_G32}
@@ -77,6 +78,9 @@ _SIGS = {
     "svdq_chain_workspace_size": [_LP, _LP, _I64, C.POINTER(_SZ)],
     "svdq_linear_forward_chain": [_LP, _LP, _P, _I64, _I64, _P, _I64, _P, _SZ, _P, _SZ, C.c_uint, _P],
     "svdq_int4_group_partials": [_LP, _P, _SZ, _I64, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P],
+    "svdq_probe_clock": [_P, C.POINTER(C.c_double)],
+    "svdq_trace_read": [_P, _I, C.POINTER(_I), C.POINTER(C.c_double)],
+    "svdq_probe_mfma_rate": [_I, _I, _P, C.POINTER(C.c_double), C.POINTER(C.c_double)],
 }
 
 _LIB = None
@@ -364,6 +368,31 @@ class SVDQLinear:
 
     def export(self, stream=None):
         return layer_export(self.layer, stream)
+
+
+def trace_read(max_records: int = 65536):
+    """Per-workgroup records of the last traced GEMM: (start wall ticks,
+    start shader cycles, end wall ticks, end shader cycles) as uint64 [n, 4],
+    and the wall-clock rate in Hz."""
+    n = C.c_int()
+    hz = C.c_double()
+    buf = np.zeros((max_records, 4), dtype=np.uint64)
+    _call("svdq_trace_read", _np_ptr(buf), int(max_records), C.byref(n), C.byref(hz))
+    return buf[:min(n.value, max_records)].copy(), hz.value
+
+
+def probe_clock(stream=None) -> float:
+    """Shader clock right now (MHz), measured on every compute unit."""
+    v = C.c_double()
+    _call("svdq_probe_clock", _stream(stream), C.byref(v))
+    return v.value
+
+
+def probe_mfma_rate(random_operands: bool, iters: int = 2000, stream=None):
+    """Sustained scaled-FP4 MFMA rate (TFLOP/s) and mean clock (MHz)."""
+    t, m = C.c_double(), C.c_double()
+    _call("svdq_probe_mfma_rate", 1 if random_operands else 0, int(iters), _stream(stream), C.byref(t), C.byref(m))
+    return t.value, m.value
 
 
 def activation_absmax(X, dtype: int, out=None, stream=None):

@@ -62,11 +62,15 @@ typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
 
 enum {
   SVDQ_FLAG_GELU = 1u,            /* apply x * Phi(x) (erf GELU) to Y before rounding */
-  SVDQ_FLAG_UNFUSED_LOWRANK = 2u  /* baseline for measuring the fusion: run the low-rank
+  SVDQ_FLAG_UNFUSED_LOWRANK = 2u, /* baseline for measuring the fusion: run the low-rank
                                      branch as separate passes (a second read of X for T,
                                      then Y is read back and rewritten with T L2 added),
                                      as an engine without the fusion would; Y is rounded
                                      twice.  svdq_linear_forward only. */
+  SVDQ_FLAG_TRACE = 4u            /* record the GEMM's per-workgroup start / end times and
+                                     shader-clock cycles (svdq_trace_read); results are
+                                     unchanged.  svdq_linear_forward, svdq_gemm_forward,
+                                     svdq_linear_forward_noalloc. */
 };
 
 #define SVDQ_MAX_RANK_CAPACITY 128
@@ -271,6 +275,36 @@ svdq_status svdq_svd_factors(const void* W_host, int64_t K, int64_t N, int64_t l
 svdq_status svdq_int4_group_partials(const svdq_layer* layer, const void* ws_dev, size_t ws_bytes, int64_t M,
                                      int64_t m0, int64_t nm, int64_t n0, int64_t nn, int64_t g0, int64_t ng,
                                      int32_t* out_dev, hipStream_t stream);
+
+/* ---------------------------------------------------- measurement hooks --- */
+
+/* The trace of the last GEMM launched with SVDQ_FLAG_TRACE on the current
+ * device: for each of its *n_records workgroups (at most 65536 are kept),
+ * four counters -- wall clock and shader clock when the workgroup started,
+ * wall clock and shader clock after its last store was issued.  The wall
+ * clock runs at *wall_hz; cycles / wall time is the shader clock the
+ * workgroup ran at.  Writes min(*n_records, max_records) records (4 x
+ * uint64 each) to host memory `records`.  Synchronizes the device.  A
+ * library-owned array per device holds the trace: traced launches that
+ * overlap on one device overwrite each other's records. */
+svdq_status svdq_trace_read(unsigned long long* records, int max_records, int* n_records, double* wall_hz);
+
+/* Shader clock of the current device right now, in MHz: a short spin on
+ * every compute unit timed by the shader-clock counter (s_memtime) and the
+ * constant-rate wall counter (s_memrealtime).  Run right after a workload,
+ * it reports the clock the power management settled on under that load.
+ * Synchronous on `stream`.  Not thread-safe against itself on one device
+ * (a lock inside serialises host threads). */
+svdq_status svdq_probe_clock(hipStream_t stream, double* mhz);
+
+/* Sustained rate of the scaled FP4 matrix instruction the MXFP4 GEMM uses
+ * (V_MFMA_SCALE_F32_32X32X64_F8F6F4, E2M1 operands): eight waves on every
+ * compute unit, `iters` x 9 independent instructions each, no memory
+ * traffic.  random_operands = 0 feeds zero codes, else pseudo-random codes
+ * (the matrix core's power, and with it the clock the chip can hold,
+ * depends on the operand bits).  tflops: achieved dense rate; mhz: the
+ * mean shader clock over the loop.  1 <= iters <= 2^24.  Synchronous. */
+svdq_status svdq_probe_mfma_rate(int random_operands, int iters, hipStream_t stream, double* tflops, double* mhz);
 
 #ifdef __cplusplus
 }
