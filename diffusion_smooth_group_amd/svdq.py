@@ -15,7 +15,9 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsvdq.so")
+# SVDQ_LIBRARY selects another build of the same library (the host-sanitizer
+# build the CPU tests use); by default the in-tree libsvdq.so
+LIB_PATH = os.environ.get("SVDQ_LIBRARY") or os.path.join(_HERE, "libsvdq.so")
 
 FMT_INT4_G64 = 0
 FMT_MXFP4_G32 = 1

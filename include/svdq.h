@@ -53,12 +53,22 @@ typedef enum {
 typedef enum {
   SVDQ_FMT_INT4_G64 = 0,     /* signed INT4 codes in [-7, 7], group 64 along K, fp16 scales */
   SVDQ_FMT_MXFP4_G32 = 1,    /* E2M1 codes, group 32 along K, e8m0 (power-of-two) scales */
-  SVDQ_FMT_INT8_W8A8 = 2     /* the 8-bit setting (SVDQuant §5.1 implementation details): signed
+  SVDQ_FMT_INT8_W8A8 = 2,    /* the 8-bit setting (SVDQuant §5.1 implementation details): signed
                                 INT8 codes in [-127, 127], one fp32 scale per output channel of
                                 the residual and, computed on the fly, per token of X_hat */
+  /* range markers (not formats): they make every int a value of the type, so
+     an unknown value passed in is reported (SVDQ_ERR_INVALID_ARG), not
+     undefined behaviour of the C++ implementation */
+  SVDQ_FMT_RANGE_MIN_ = -2147483647 - 1,
+  SVDQ_FMT_RANGE_MAX_ = 2147483647
 } svdq_format;
 
-typedef enum { SVDQ_F16 = 0, SVDQ_BF16 = 1 } svdq_dtype;
+typedef enum {
+  SVDQ_F16 = 0,
+  SVDQ_BF16 = 1,
+  SVDQ_DTYPE_RANGE_MIN_ = -2147483647 - 1,   /* range markers, as for svdq_format */
+  SVDQ_DTYPE_RANGE_MAX_ = 2147483647
+} svdq_dtype;
 
 enum {
   SVDQ_FLAG_GELU = 1u,            /* apply x * Phi(x) (erf GELU) to Y before rounding */
