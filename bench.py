@@ -58,7 +58,7 @@ def parse():
                     help="instead of the headline line, time the forward three ways -- W4A4 only (rank 0), "
                          "fused low-rank branch, low-rank branch as separate passes -- and print their overheads")
     ap.add_argument("--chain-study", action="store_true",
-                    help="instead of the headline line, time the FLUX MLP pair (fc1 + GELU -> fc2, MXFP4) with "
+                    help="instead of the headline line, time the FLUX MLP pair (fc1 + GELU -> fc2; --fmt mxfp4 or int4) with "
                          "fc2's activation pass as its own kernel and chained into fc1's GEMM epilogue")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the headline line, print one JSON record per (config, shape, format) over "
@@ -234,7 +234,7 @@ def lowrank_study(args):
 
 
 def chain_study(args):
-    """The MLP pair fc1 (+GELU) -> fc2 two ways: unchained (fc1 writes Y1,
+    """The MLP pair fc1 (+GELU) -> fc2 (--fmt mxfp4 or int4) two ways: unchained (fc1 writes Y1,
     fc2's activation kernel reads it back) and chained (fc2's codes, scales
     and down-projection come out of fc1's GEMM epilogue; Y1 is not stored)."""
     import ctypes as C
@@ -243,7 +243,8 @@ def chain_study(args):
     from diffusion_smooth_group_amd import workloads as wl
     fc1, fc2 = wl.config_shapes(3)
     M, K, H = fc1.M, fc1.K, fc1.N
-    dt, fmt = S.BF16, S.FMT_MXFP4_G32
+    dt = S.BF16
+    fmt = {"mxfp4": S.FMT_MXFP4_G32, "int4": S.FMT_INT4_G64}[args.fmt]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d1 = wl.generate(fc1)
@@ -318,7 +319,8 @@ def chain_study(args):
     flops = 2.0 * M * K * H * 2
     print(json.dumps({
         "study": "MLP pair fc1 (+GELU) -> fc2: fc2's activation pass as its own kernel vs chained into fc1's epilogue",
-        "workload": f"flux_mlp_{M}x{K}x{H}x{K}", "format": "mxfp4_g32", "rank": args.rank, "activation_dtype": "bf16",
+        "workload": f"flux_mlp_{M}x{K}x{H}x{K}", "format": FMT_NAMES[args.fmt], "rank": args.rank,
+        "activation_dtype": "bf16",
         "rotating_buffer_sets": nrot, "steps": args.steps, "rounds": 3,
         "t_unchained_us": round(tu, 2), "t_chained_us": round(tc, 2),
         "saving_pct": round(100.0 * (tu - tc) / tu, 1),

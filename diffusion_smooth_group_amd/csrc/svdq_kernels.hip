@@ -128,6 +128,57 @@ __device__ __forceinline__ int e8m0_slow(float a) {      // any a >= 0
 }
 __device__ __forceinline__ bool e8m0_needs_slow(float a) { return (__float_as_uint(a) >> 23) < 3u; }
 
+// INT4 group quantization of one 128-deep K step of 16 tokens, in the
+// activation fragment layout: lane l = m + 16q holds token m and, in chunk
+// c = 0..3, the smoothed values xh[c][0..7] of k in [32c + 8q, +8), with am[c]
+// their maximum magnitude; a 64-group is chunks 2g, 2g + 1 of the token's
+// four lanes, whose maxima meet through quad_max.  Writes the lane's 16 code
+// bytes (element order of the fragment: chunk c in bytes [4c, 4c + 4)) and
+// the fp16 scale bits of the two groups.  The activation kernel and the
+// chained GEMM epilogue both quantize through this function.
+__device__ __forceinline__ void int4_quant_step(const float (&xh)[4][8], const float (&am)[4], unsigned (&d)[4],
+                                                unsigned (&sh)[2]) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const float a = quad_max(fmaxf(am[2 * g], am[2 * g + 1]));
+    const float sc = fminf(a / 7.0f, 65504.0f);
+    sh[g] = f2h<SVDQ_F16>(sc);
+    const float s32 = h2f<SVDQ_F16>(sh[g]);
+    // The code is rint(fl(x / s)).  x * fl(1/s) is within 1.5 ulp of
+    // fl(x / s), below 2^-19 wherever |x / s| < 10.5 (larger values
+    // clamp to 7 either way), so the two roundings can only differ when
+    // it lies within 2^-18 of a half-integer; such lanes redo the group
+    // with the correctly rounded division.
+    const float inv = s32 != 0.0f ? 1.0f / s32 : 0.0f;
+    bool near = false;
+    float r[2][8];
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float qv = xh[2 * g + cc][e] * inv;
+        r[cc][e] = rintf(qv);
+        near |= fabsf(qv - r[cc][e]) >= 0.5f - 0x1p-18f;
+      }
+    if (__builtin_expect(near, 0)) {
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[cc][e] = s32 != 0.0f ? rintf(xh[2 * g + cc][e] / s32) : 0.0f;
+    }
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      unsigned v = 0u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float rc = __builtin_amdgcn_fmed3f(r[cc][e], -7.0f, 7.0f);   // clamp, one v_med3_f32
+        v |= (unsigned(int(rc)) & 0xFu) << (4 * e);
+      }
+      d[2 * g + cc] = v;
+    }
+  }
+}
+
 // ------------------------------------------------------------------- k1_act
 struct K1Params {
   const uint16_t* X;
@@ -290,45 +341,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     if constexpr (FMT == SVDQ_FMT_INT4_G64) {
       unsigned d[4];
       unsigned sh[2];
-#pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        const float a = quad_max(fmaxf(am[2 * g], am[2 * g + 1]));
-        const float sc = fminf(a / 7.0f, 65504.0f);
-        sh[g] = f2h<SVDQ_F16>(sc);
-        const float s32 = h2f<SVDQ_F16>(sh[g]);
-        // The code is rint(fl(x / s)).  x * fl(1/s) is within 1.5 ulp of
-        // fl(x / s), below 2^-19 wherever |x / s| < 10.5 (larger values
-        // clamp to 7 either way), so the two roundings can only differ when
-        // it lies within 2^-18 of a half-integer; such lanes redo the group
-        // with the correctly rounded division.
-        const float inv = s32 != 0.0f ? 1.0f / s32 : 0.0f;
-        bool near = false;
-        float r[2][8];
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float qv = xh[2 * g + cc][e] * inv;
-            r[cc][e] = rintf(qv);
-            near |= fabsf(qv - r[cc][e]) >= 0.5f - 0x1p-18f;
-          }
-        if (__builtin_expect(near, 0)) {
-#pragma unroll
-          for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) r[cc][e] = s32 != 0.0f ? rintf(xh[2 * g + cc][e] / s32) : 0.0f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-          unsigned v = 0u;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float rc = __builtin_amdgcn_fmed3f(r[cc][e], -7.0f, 7.0f);   // clamp, one v_med3_f32
-            v |= (unsigned(int(rc)) & 0xFu) << (4 * e);
-          }
-          d[2 * g + cc] = v;
-        }
-      }
+      int4_quant_step(xh, am, d, sh);
       uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
       *reinterpret_cast<u32x4*>(frag + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
       if (q == 0)
@@ -474,6 +487,17 @@ struct K2Params {
   int64_t ldy, M, N, K;
   int slots, nchunks, nchunks16;
   unsigned long long* trace;   // GEMM trace records (SVDQ_FLAG_TRACE) or null
+  // Epilogue chaining of INT4 layers (k2_int4 with CHAIN): the next layer's
+  // 1/lambda over this layer's N columns, its L1x (activation-kernel
+  // tiling), its workspace codes and scales (written here), and fp32 partial
+  // down-projections [N / 128][nx_Mp][nx_slots], one slab per 128-column tile
+  const float* nx_invlam;
+  const uint16_t* nx_l1x;
+  uint8_t* nx_xq;
+  uint8_t* nx_sx;
+  float* nx_tp;
+  int64_t nx_Mp;
+  int nx_slots, nx_njt;
 };
 
 __device__ __forceinline__ i32x4 widen_nibbles(unsigned d0, unsigned d1) {
@@ -525,6 +549,67 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return __builtin_fmaf(-fabsf(x), e, __builtin_amdgcn_fmed3f(x, 0.0f, 3.40282347e38f));   // max(x, 0)
 }
 
+// Epilogue chaining for INT4 layers (the next layer is INT4 too): the
+// workgroup's staged 128 x 128 output tile -- the exact 16-bit bits this
+// layer stores -- is one 128-deep K step of the next layer for 128 tokens.
+// Wave w takes tokens 32w .. 32w + 31 in two 16-token sub-tiles with the
+// activation kernel's INT4 lane layout (lane m + 16q holds k in
+// [32c + 8q, +8) of chunk c): smoothing by the next layer's 1/lambda, codes
+// and scales through int4_quant_step (so they are the activation kernel's
+// bit for bit), and the down-projection over this step on the 16 x 16 x 32
+// MFMA with the raw 16-bit values, written as fp32 to this column tile's
+// slab (k_tfin sums the slabs in a fixed order).
+template <int DT>
+__device__ __forceinline__ void int4_chain_epilogue(const K2Params& p, const uint8_t* stage, int wave, int lane) {
+  constexpr int OP = 64 * 2 + 16;                 // bytes per staged row (as in k2_int4)
+  const int m = lane & 15, q = lane >> 4;
+  const int s2 = blockIdx.x;                      // the next layer's K step: this tile's 128 columns
+  const int nst2 = int(p.N / KSTEP);              // the next layer's K steps
+  const int64_t mw0 = int64_t(blockIdx.y) * 128;
+  const u32x4* l1 = reinterpret_cast<const u32x4*>(p.nx_l1x) + (size_t(s2) * (p.nx_slots / 16)) * 4 * 64 + lane;
+  const int njc = p.nx_njt > 0 ? p.nx_njt - 1 : 0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int t = 32 * wave + 16 * u + m;         // token within the workgroup tile
+    const int wm = t >> 6, row = t & 63;
+    u32x4 xq[4];
+    float xh[4][8], am[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int wn = c >> 1, col = 32 * (c & 1) + 8 * q;
+      xq[c] = *reinterpret_cast<const u32x4*>(stage + (wn + 2 * wm) * (64 * OP) + row * OP + col * 2);
+      const int k = s2 * KSTEP + 32 * c + 8 * q;
+      const f32x4 il0 = *reinterpret_cast<const f32x4*>(p.nx_invlam + k);
+      const f32x4 il1 = *reinterpret_cast<const f32x4*>(p.nx_invlam + k + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const unsigned w = xq[c][e];
+        const f32x4& il = e < 2 ? il0 : il1;
+        xh[c][2 * e] = h2f<DT>(w & 0xFFFFu) * il[(2 * e) & 3];
+        xh[c][2 * e + 1] = h2f<DT>(w >> 16) * il[(2 * e + 1) & 3];
+      }
+      am[c] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) am[c] = fmaxf(am[c], fabsf(xh[c][e]));
+    }
+    unsigned d[4], sh[2];
+    int4_quant_step(xh, am, d, sh);
+    const int64_t mt2 = (mw0 + 32 * wave + 16 * u) / 16;
+    *reinterpret_cast<u32x4*>(p.nx_xq + (size_t(mt2) * nst2 + s2) * svdq::FRAG_BYTES + lane * 16) =
+        u32x4{d[0], d[1], d[2], d[3]};
+    if (q == 0) reinterpret_cast<unsigned*>(p.nx_sx)[(size_t(mt2) * nst2 + s2) * 16 + m] = sh[0] | (sh[1] << 16);
+    // partial T[token][16 jt + 4q + i] over this step
+    float* tp = p.nx_tp + (size_t(s2) * p.nx_Mp + size_t(mw0 + t)) * p.nx_slots + 4 * q;
+    for (int jt = 0; jt < p.nx_njt; ++jt) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int jj = jt < njc ? jt : njc;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma16<DT>(l1[(jj * 4 + c) * 64], xq[c], acc);
+      *reinterpret_cast<f32x4*>(tp + 16 * jt) = acc;
+    }
+  }
+}
+
 // INT4 GEMM.  One workgroup = 128 output columns x 128 tokens; 4 waves in a
 // 2 x 2 grid, each 64 x 64 (4 x 4 MFMA tiles of 16 x 16).  Per 64-group the
 // integer MFMA gives the exact partial P_g (the nibbles are widened to
@@ -540,7 +625,7 @@ __device__ __forceinline__ float gelu_erf(float x) {
 // operands and scales are buffer loads with the lane's offset fixed and the
 // step's offset in scalar registers (no per-step address arithmetic on the
 // VALU), each step loaded one step ahead, and several waves share a SIMD.
-template <int DT, bool GELU>
+template <int DT, bool GELU, bool CHAIN = false>
 __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   trace_mark(p.trace, 0);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -674,12 +759,18 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
     }
   }
   SVDQ_WAIT_LGKM0();
-  // 8 rows of 128 bytes per instruction: lane l takes row l / 8, piece l % 8
+  if (!CHAIN || p.Y != nullptr) {
+    // 8 rows of 128 bytes per instruction: lane l takes row l / 8, piece l % 8
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int row = 8 * it + (lane >> 3), col = (lane & 7) * 8;
-    const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OP + col * 2);
-    if (m0 + row < p.M) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col));
+    for (int it = 0; it < 8; ++it) {
+      const int row = 8 * it + (lane >> 3), col = (lane & 7) * 8;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * OP + col * 2);
+      if (m0 + row < p.M) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + col));
+    }
+  }
+  if constexpr (CHAIN) {
+    __syncthreads();                      // every wave's tile is staged
+    int4_chain_epilogue<DT>(p, &ostage[0][0], wave, lane);
   }
   trace_mark(p.trace, 2);
 }
@@ -1947,7 +2038,7 @@ struct TfinParams {
   int slots, nparts, ncols4;
 };
 
-template <int DT>
+template <int DT, int FMT>
 __global__ __launch_bounds__(256) void k_tfin(TfinParams p) {
   __shared__ f32x4 part[3][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1969,11 +2060,21 @@ __global__ __launch_bounds__(256) void k_tfin(TfinParams p) {
     s += part[0][lane];
     s += part[1][lane];
     s += part[2][lane];
-    // MXFP4 low-rank layout: 32-row tiles, 16-rank chunks, lane (row % 32) + 32 (j % 16 >= 8)
-    const int j = 4 * j4, c = j / 16, jj = j % 16;
-    const int64_t ln = (m % 32) + 32 * (jj / 8);
-    *reinterpret_cast<u32x2*>(p.t + (((m / 32) * (p.slots / 16) + c) * 64 + ln) * 8 + (jj % 8)) =
-        u32x2{pack2<DT>(s[0], s[1]), pack2<DT>(s[2], s[3])};
+    const int j = 4 * j4;
+    uint16_t* dst;
+    if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
+      // MXFP4 low-rank layout: 32-row tiles, 16-rank chunks, lane (row % 32) + 32 (j % 16 >= 8)
+      const int c = j / 16, jj = j % 16;
+      const int64_t ln = (m % 32) + 32 * (jj / 8);
+      dst = p.t + (((m / 32) * (p.slots / 16) + c) * 64 + ln) * 8 + (jj % 8);
+    } else {
+      // INT4 low-rank layout: 16-row tiles, 32-rank chunks; the activation
+      // kernel's lane (m, q) of 16-rank tile jt holds ranks 16 jt + 4q .. + 3
+      const int jt = j / 16, q = (j % 16) / 4;
+      const int64_t ln = (m % 16) + 16 * (2 * (jt & 1) + (q >> 1));
+      dst = p.t + (((m / 16) * (p.slots / 32) + (jt >> 1)) * 64 + ln) * 8 + 4 * (q & 1);
+    }
+    *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<DT>(s[0], s[1]), pack2<DT>(s[2], s[3])};
   }
 }
 
@@ -2245,6 +2346,8 @@ K2Params k2_params(const svdq_layer* L, int64_t M, void* Y_dev, int64_t ldy, con
   kp.nchunks = int(svdq::ceil_div(ra, 32));
   kp.nchunks16 = int(svdq::ceil_div(ra, 16));
   kp.trace = nullptr;
+  kp.nx_invlam = nullptr; kp.nx_l1x = nullptr; kp.nx_xq = nullptr; kp.nx_sx = nullptr; kp.nx_tp = nullptr;
+  kp.nx_Mp = 0; kp.nx_slots = 0; kp.nx_njt = 0;
   return kp;
 }
 
@@ -2329,12 +2432,17 @@ svdq_status check_chain(const svdq_layer* A, const svdq_layer* B) {
   if (st != SVDQ_OK || (st = check_device_layer(B)) != SVDQ_OK) return st;
   if (A->dtype != B->dtype) return SVDQ_ERR_INVALID_ARG;
   if (A->N != B->K) return SVDQ_ERR_SHAPE;
-  if (A->fmt != SVDQ_FMT_MXFP4_G32 || B->fmt != SVDQ_FMT_MXFP4_G32) return SVDQ_ERR_UNSUPPORTED;
+  // pairs of one 4-bit format: MXFP4 -> MXFP4 or INT4 -> INT4
+  const bool mx = A->fmt == SVDQ_FMT_MXFP4_G32 && B->fmt == SVDQ_FMT_MXFP4_G32;
+  const bool i4 = A->fmt == SVDQ_FMT_INT4_G64 && B->fmt == SVDQ_FMT_INT4_G64;
+  if (!mx && !i4) return SVDQ_ERR_UNSUPPORTED;
   return SVDQ_OK;
 }
 size_t chain_partials_offset(const svdq::WsOffsets& w) { return svdq::align256(w.total); }
+// output columns of `first` per partial slab: the GEMM's workgroup tile width
+int64_t chain_slab_cols(const svdq_layer* A) { return A->fmt == SVDQ_FMT_INT4_G64 ? 128 : 256; }
 size_t chain_partials_bytes(const svdq_layer* A, const svdq_layer* B, const svdq::WsOffsets& w) {
-  return size_t(svdq::ceil_div(A->N, 256)) * size_t(w.Mp) * size_t(B->rank_slots) * 4;
+  return size_t(svdq::ceil_div(A->N, chain_slab_cols(A))) * size_t(w.Mp) * size_t(B->rank_slots) * 4;
 }
 
 }  // namespace
@@ -2369,31 +2477,58 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   uint8_t* wsn = static_cast<uint8_t*>(ws_next_dev);
   const uint8_t* nblob = static_cast<const uint8_t*>(next->blob);
-  run_k1(first, X_dev, M, ldx, ws, w, K1_BOTH, stream);
-  MxParams mp = mx_params(k2_params(first, M, Y_dev, ldy, ws, w, true), w);
-  mp.nx_invlam = reinterpret_cast<const float*>(nblob + next->off_invlam);
-  mp.nx_l1x = reinterpret_cast<const uint16_t*>(nblob + next->off_l1x);
-  mp.nx_xq = wsn + wn.xq;
-  mp.nx_sx = wsn + wn.sx;
-  mp.nx_tp = reinterpret_cast<float*>(ws + chain_partials_offset(w));
-  mp.nx_Mp = w.Mp;
-  mp.nx_slots = next->rank_slots;
-  mp.nx_njt = int(svdq::ceil_div(next->rank_active, 16));
   const bool gelu = (flags & SVDQ_FLAG_GELU) != 0u;
-  if (first->dtype == SVDQ_BF16) launch_k2_mx_chain<SVDQ_BF16>(mp, gelu, stream);
-  else launch_k2_mx_chain<SVDQ_F16>(mp, gelu, stream);
-  if (mp.nx_njt > 0) {
+  const bool i4 = first->fmt == SVDQ_FMT_INT4_G64;
+  run_k1(first, X_dev, M, ldx, ws, w, K1_BOTH, stream);
+  K2Params kp = k2_params(first, M, Y_dev, ldy, ws, w, true);
+  kp.nx_invlam = reinterpret_cast<const float*>(nblob + next->off_invlam);
+  kp.nx_l1x = reinterpret_cast<const uint16_t*>(nblob + next->off_l1x);
+  kp.nx_xq = wsn + wn.xq;
+  kp.nx_sx = wsn + wn.sx;
+  kp.nx_tp = reinterpret_cast<float*>(ws + chain_partials_offset(w));
+  kp.nx_Mp = w.Mp;
+  kp.nx_slots = next->rank_slots;
+  // T column tiles of 16: INT4 fills whole 32-rank chunks (its T layout)
+  kp.nx_njt = i4 ? 2 * int(svdq::ceil_div(next->rank_active, 32)) : int(svdq::ceil_div(next->rank_active, 16));
+  if (i4) {
+    const dim3 grid(unsigned(kp.N / 128), unsigned(w.Mp / 128));
+    if (first->dtype == SVDQ_BF16) {
+      if (gelu) hipLaunchKernelGGL((k2_int4<SVDQ_BF16, true, true>), grid, dim3(256), 0, stream, kp);
+      else hipLaunchKernelGGL((k2_int4<SVDQ_BF16, false, true>), grid, dim3(256), 0, stream, kp);
+    } else {
+      if (gelu) hipLaunchKernelGGL((k2_int4<SVDQ_F16, true, true>), grid, dim3(256), 0, stream, kp);
+      else hipLaunchKernelGGL((k2_int4<SVDQ_F16, false, true>), grid, dim3(256), 0, stream, kp);
+    }
+  } else {
+    MxParams mp = mx_params(kp, w);
+    mp.nx_invlam = kp.nx_invlam;
+    mp.nx_l1x = kp.nx_l1x;
+    mp.nx_xq = kp.nx_xq;
+    mp.nx_sx = kp.nx_sx;
+    mp.nx_tp = kp.nx_tp;
+    mp.nx_Mp = kp.nx_Mp;
+    mp.nx_slots = kp.nx_slots;
+    mp.nx_njt = kp.nx_njt;
+    if (first->dtype == SVDQ_BF16) launch_k2_mx_chain<SVDQ_BF16>(mp, gelu, stream);
+    else launch_k2_mx_chain<SVDQ_F16>(mp, gelu, stream);
+  }
+  if (kp.nx_njt > 0) {
     TfinParams tf;
-    tf.tp = mp.nx_tp;
+    tf.tp = kp.nx_tp;
     tf.t = reinterpret_cast<uint16_t*>(wsn + wn.t);
     tf.Mp = w.Mp;
     tf.slots = next->rank_slots;
-    tf.nparts = mp.tiles_n;
-    tf.ncols4 = 4 * mp.nx_njt;
+    tf.nparts = int(svdq::ceil_div(first->N, chain_slab_cols(first)));
+    tf.ncols4 = 4 * kp.nx_njt;
     const int64_t n = w.Mp * tf.ncols4;
     const dim3 grid(unsigned((n + 63) / 64));
-    if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16>), grid, dim3(256), 0, stream, tf);
-    else hipLaunchKernelGGL((k_tfin<SVDQ_F16>), grid, dim3(256), 0, stream, tf);
+    if (i4) {
+      if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
+      else hipLaunchKernelGGL((k_tfin<SVDQ_F16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
+    } else {
+      if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
+      else hipLaunchKernelGGL((k_tfin<SVDQ_F16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
+    }
   }
   return launch_ok();
 }

@@ -225,14 +225,16 @@ svdq_status svdq_gemm_forward(const svdq_layer* layer, int64_t M, void* Y_dev, i
  * runs across a layer boundary: the 4-bit GEMM of `first` computes, in its
  * epilogue and from the 16-bit output bits it would store, `next`'s
  * smoothing, group quantization (codes and scales into ws_next_dev) and
- * fp32 partial down-projections (one slab per 256 output columns of `first`,
- * in ws_dev); a small kernel then sums the slabs in a fixed order and rounds
- * T once into ws_next_dev.  The activation pass of `next` over `first`'s
- * output is gone; svdq_gemm_forward(next, M, ..., ws_next_dev, ...) finishes
- * `next`.  Codes and scales are identical to what svdq_quantize_activations
- * writes for that output; T differs only in fp32 summation order.
- * Requires: both layers MXFP4 (else SVDQ_ERR_UNSUPPORTED), the same dtype
- * (else SVDQ_ERR_INVALID_ARG), first->N == next->K (else SVDQ_ERR_SHAPE).
+ * fp32 partial down-projections (one slab per GEMM column tile of `first`:
+ * 256 output columns for MXFP4, 128 for INT4, in ws_dev); a small kernel
+ * then sums the slabs in a fixed order and rounds T once into ws_next_dev.
+ * The activation pass of `next` over `first`'s output is gone;
+ * svdq_gemm_forward(next, M, ..., ws_next_dev, ...) finishes `next`.  Codes
+ * and scales are identical to what svdq_quantize_activations writes for that
+ * output; T differs only in fp32 summation order.
+ * Requires: both layers MXFP4 or both INT4 (else SVDQ_ERR_UNSUPPORTED), the
+ * same dtype (else SVDQ_ERR_INVALID_ARG), first->N == next->K (else
+ * SVDQ_ERR_SHAPE).
  * X_dev as for svdq_linear_forward on `first`; Y_dev may be NULL (the
  * output of `first` is then not stored; else as for svdq_linear_forward);
  * flags: SVDQ_FLAG_GELU for `first`.  ws_dev: >= svdq_chain_workspace_size
