@@ -386,32 +386,29 @@ def sweep(args):
                 wss = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(nrot)]
                 flags = S.FLAG_GELU if gelu else 0
 
-                def step(i, ev=None):
+                def step(i):
                     j = i % nrot
-                    if ev is not None:
-                        ev[0].record(stream)
                     rc = lib.svdq_quantize_activations(C.byref(layers[j]), S._t_ptr(Xs[j]), M, K, S._t_ptr(wss[j]),
                                                        wsb, sh)
                     if rc != 0:
                         raise S.SvdqError("svdq_quantize_activations", rc)
-                    if ev is not None:
-                        ev[1].record(stream)
                     rc = lib.svdq_gemm_forward(C.byref(layers[j]), M, S._t_ptr(Ys[j]), N, S._t_ptr(wss[j]), wsb,
                                                flags, sh)
                     if rc != 0:
                         raise S.SvdqError("svdq_gemm_forward", rc)
-                    if ev is not None:
-                        ev[2].record(stream)
                 for i in range(warm):
                     step(i)
-                evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
                 torch.cuda.synchronize()
+                # each kernel timed from its own dispatch timestamps
+                S.timing_start(2 * steps)
                 for i in range(steps):
-                    step(i, evs[i])
+                    step(i)
                 torch.cuda.synchronize()
-                t1 = float(np.median([e[0].elapsed_time(e[1]) for e in evs]) * 1e3)
-                t2 = float(np.median([e[1].elapsed_time(e[2]) for e in evs]) * 1e3)
-                tf = float(np.median([e[0].elapsed_time(e[2]) for e in evs]) * 1e3)
+                kinds, kus = S.timing_stop(4 * steps)
+                k1u, k2u = kus[kinds == S.KERNEL_ACT], kus[kinds == S.KERNEL_GEMM]
+                t1 = float(np.median(k1u))
+                t2 = float(np.median(k2u))
+                tf = float(np.median(k1u + k2u))
                 ops = 2.0 * M * K * N
                 peak = PEAK_TFLOPS[fmt_name]
                 b2 = k2_bytes(M, K, N, ra, fmt_name)
@@ -536,20 +533,25 @@ def main():
     wall = time.perf_counter() - tw0
     ms_step = ev0.elapsed_time(ev1) / args.steps
 
-    # ---- the same forward loop again (after the timed region), each step as
-    # its two kernels -- svdq_quantize_activations and svdq_gemm_forward, the
-    # launches svdq_linear_forward makes -- with HIP events on the launch
-    # stream before, between and after them: per-kernel durations inside
-    # forwards, K1 + K2 = the forward by construction
+    # ---- the same forward loop again, each kernel launched with an event
+    # pair that takes that kernel's own dispatch begin / end timestamps
+    # (svdq_timing_start: hipExtLaunchKernel, nothing added to the stream
+    # between kernels), so K1 + K2 <= the forward by construction
     n_inst = max(args.steps, args.kernel_iters)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_inst)]
-    for i in range(n_inst):
-        evs[i][0].record(stream)
-        k1(i)
-        evs[i][1].record(stream)
-        k2(i)
-        evs[i][2].record(stream)
+    ev2, ev3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    S.timing_start(2 * n_inst)
+    ev2.record(stream)
+    for i in range(n_inst):
+        fwd(i)
+    ev3.record(stream)
+    torch.cuda.synchronize()
+    kinds, kus = S.timing_stop(4 * n_inst)
+    ms_step_kt = ev2.elapsed_time(ev3) / n_inst
+    t_k1 = kus[kinds == S.KERNEL_ACT]
+    t_k2 = kus[kinds == S.KERNEL_GEMM]
+    if len(t_k1) != n_inst or len(t_k2) != n_inst:
+        raise RuntimeError(f"kernel timing recorded {len(t_k1)} / {len(t_k2)} launches, expected {n_inst}")
     sclk_after = S.probe_clock(stream)      # a light kernel right after the loop
     # three more forwards with the GEMM traced (per-workgroup wall and
     # shader-clock counters): the clock the GEMM itself ran at
@@ -574,8 +576,6 @@ def main():
                        "wg_us": np.percentile(wg_ticks / hz * 1e6, [10, 50, 90]).tolist(),
                        "workgroups": int(len(r))})
     tr = sorted(traces, key=lambda t: t["span_us"])[1]          # the median of the three by span
-    t_k1 = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e3
-    t_k2 = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e3
     t_fw = t_k1 + t_k2
 
     def stats(t):
@@ -620,15 +620,16 @@ def main():
                      "traffic": measured_traffic(f"flux_{args.workload}_{M}x{K}x{N}", fmt_name),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": k2_bytes(M, K, N, args.rank, fmt_name),
-                     "time_source": "mean K2 duration inside the forward loop (HIP events around each kernel)",
+                     "time_source": "mean K2 duration over a forward loop, each launch timed by events bound to the "
+                                    "kernel's own dispatch timestamps (hipExtLaunchKernel)",
                      "frac_of_sustained_fp4_rate": round(k2_tflops / ceil["random_tflops"], 4)
                      if fmt_name == "mxfp4_g32" else None,
                      "frac_at_traced_clock": round(k2_tflops / (peak * tr["sclk_mhz"] / 2400.0), 4)},
         "k1_roofline": {"bound": "hbm", "kernel": "k1_act", "achieved": round(k1_gbs, 1), "peak": HBM_PEAK_GBS,
                         "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                         "algorithmic_bytes_per_launch": k1_bytes(M, K, args.rank, fmt_name)},
-        "kernel_us": {"k1_act": stats(t_k1), "k2_gemm": stats(t_k2), "forward": stats(t_fw),
-                      "launches": n_inst},
+        "kernel_us": {"k1_act": stats(t_k1), "k2_gemm": stats(t_k2), "k1_plus_k2": stats(t_fw),
+                      "launches": n_inst, "forward_loop_us_per_step": round(ms_step_kt * 1e3, 2)},
         "sclk_mhz": {"idle_probe": round(sclk_idle, 1), "probe_after_forward_loop": round(sclk_after, 1),
                      "gemm_traced": round(tr["sclk_mhz"], 1)},
         "k2_trace": {"workgroups": tr["workgroups"], "span_us": round(tr["span_us"], 2),

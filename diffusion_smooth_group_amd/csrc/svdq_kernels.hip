@@ -22,9 +22,11 @@
 // output columns n), the activation fragment is "B" (columns = tokens m), so
 // each lane ends with 4 consecutive n of one token and stores 8 bytes.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "svdq.h"
 #include "svdq_layout.h"
@@ -2123,6 +2125,32 @@ __global__ __launch_bounds__(256) void k_absmax(const uint16_t* X, int64_t M, in
 
 inline svdq_status launch_ok() { return hipGetLastError() == hipSuccess ? SVDQ_OK : SVDQ_ERR_HIP; }
 
+// Kernel timing (svdq_timing_start / svdq_timing_stop): while it is on for a
+// host thread, that thread's activation-kernel, GEMM and low-rank-pass
+// launches go through hipExtLaunchKernel with an event pair of their own,
+// which takes the kernel's own dispatch begin / end timestamps -- nothing is
+// added to the stream between kernels.
+struct KernelTiming {
+  bool on = false;
+  std::vector<hipEvent_t> ev;   // begin, end per launch slot
+  std::vector<int> kind;        // svdq_kernel_kind of the launch in each used slot
+  size_t used = 0;
+};
+thread_local KernelTiming t_timing;
+
+template <typename F, typename... A>
+void launch(svdq_kernel_kind kind, F kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t st, A... args) {
+  KernelTiming& t = t_timing;
+  if (t.on && t.used < t.kind.size()) {
+    hipEvent_t b = t.ev[2 * t.used], e = t.ev[2 * t.used + 1];
+    t.kind[t.used++] = int(kind);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, b, e, 0u, args...);
+  } else {
+    void* a[] = {static_cast<void*>(&args)...};
+    (void)hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, a, lds, st);
+  }
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 template <int FMT, int DT>
@@ -2132,17 +2160,17 @@ void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const size_t il_bytes = il ? size_t((kp.K + 255) & ~int64_t(255)) * 4 : 0;
   auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
   if (kp.njt == 0) {
-    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 0, true>), grid, block, il_bytes, st, kp);
-    else hipLaunchKernelGGL((k1_act<FMT, DT, 0, false>), grid, block, 0, st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, true>), grid, block, il_bytes, st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, false>), grid, block, 0, st, kp);
   } else if (kp.njt <= 2) {
-    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 2, true>), grid, block, il_bytes + red_bytes(2), st, kp);
-    else hipLaunchKernelGGL((k1_act<FMT, DT, 2, false>), grid, block, red_bytes(2), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, true>), grid, block, il_bytes + red_bytes(2), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false>), grid, block, red_bytes(2), st, kp);
   } else if (kp.njt <= 4) {
-    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, 4, true>), grid, block, il_bytes + red_bytes(4), st, kp);
-    else hipLaunchKernelGGL((k1_act<FMT, DT, 4, false>), grid, block, red_bytes(4), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, true>), grid, block, il_bytes + red_bytes(4), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false>), grid, block, red_bytes(4), st, kp);
   } else {
-    if (il) hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, true>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
-    else hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, false>), grid, block, red_bytes(MAXJT), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, true>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false>), grid, block, red_bytes(MAXJT), st, kp);
   }
 }
 
@@ -2151,27 +2179,27 @@ template <int FMT, int DT>
 void launch_k1_proj(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
   auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
-  if (kp.njt <= 2) hipLaunchKernelGGL((k1_act<FMT, DT, 2, false, false>), grid, block, red_bytes(2), st, kp);
-  else if (kp.njt <= 4) hipLaunchKernelGGL((k1_act<FMT, DT, 4, false, false>), grid, block, red_bytes(4), st, kp);
-  else hipLaunchKernelGGL((k1_act<FMT, DT, MAXJT, false, false>), grid, block, red_bytes(MAXJT), st, kp);
+  if (kp.njt <= 2) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false, false>), grid, block, red_bytes(2), st, kp);
+  else if (kp.njt <= 4) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false, false>), grid, block, red_bytes(4), st, kp);
+  else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false, false>), grid, block, red_bytes(MAXJT), st, kp);
 }
 
 template <int DT>
 void launch_k1_w8(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
-  if (kp.njt == 0) hipLaunchKernelGGL((k1_w8<DT, 0>), grid, block, 0, st, kp);
-  else if (kp.njt == 1) hipLaunchKernelGGL((k1_w8<DT, 1>), grid, block, 0, st, kp);
-  else if (kp.njt <= 2) hipLaunchKernelGGL((k1_w8<DT, 2>), grid, block, 0, st, kp);
-  else if (kp.njt <= 4) hipLaunchKernelGGL((k1_w8<DT, 4>), grid, block, 0, st, kp);
-  else hipLaunchKernelGGL((k1_w8<DT, MAXJT>), grid, block, 0, st, kp);
+  if (kp.njt == 0) launch(SVDQ_KERNEL_ACT, (k1_w8<DT, 0>), grid, block, 0, st, kp);
+  else if (kp.njt == 1) launch(SVDQ_KERNEL_ACT, (k1_w8<DT, 1>), grid, block, 0, st, kp);
+  else if (kp.njt <= 2) launch(SVDQ_KERNEL_ACT, (k1_w8<DT, 2>), grid, block, 0, st, kp);
+  else if (kp.njt <= 4) launch(SVDQ_KERNEL_ACT, (k1_w8<DT, 4>), grid, block, 0, st, kp);
+  else launch(SVDQ_KERNEL_ACT, (k1_w8<DT, MAXJT>), grid, block, 0, st, kp);
 }
 
 // (the GEMM launchers return the number of workgroups they launch)
 template <int DT>
 unsigned launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t st) {
   dim3 grid(unsigned(kp.N / 128), unsigned(Mp / 128));
-  if (gelu) hipLaunchKernelGGL((k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
-  else hipLaunchKernelGGL((k2_int4<DT, false>), grid, dim3(256), 0, st, kp);
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_int4<DT, true>), grid, dim3(256), 0, st, kp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_int4<DT, false>), grid, dim3(256), 0, st, kp);
   return grid.x * grid.y;
 }
 
@@ -2195,8 +2223,8 @@ template <int DT, bool I8 = false>
 unsigned launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   const MxParams mp = mx_params(kp, w);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
-  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
-  else hipLaunchKernelGGL((k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
   return T;
 }
 
@@ -2206,8 +2234,8 @@ unsigned launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, 
   mp.tiles_n = int(svdq::ceil_div(kp.N, C::TN));
   mp.tiles_m = int(svdq::ceil_div(w.Mp, C::TM));
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
-  if (gelu) hipLaunchKernelGGL((k2_mx8<DT, true, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
-  else hipLaunchKernelGGL((k2_mx8<DT, false, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, true, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, false, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
   return T;
 }
 
@@ -2228,16 +2256,16 @@ unsigned launch_k2_mx4(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, 
 template <int DT>
 void launch_k2_mx_chain(const MxParams& mp, bool gelu, hipStream_t st) {
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
-  if (gelu) hipLaunchKernelGGL((k2_mx<DT, true, true>), dim3(T), dim3(256), 0, st, mp);
-  else hipLaunchKernelGGL((k2_mx<DT, false, true>), dim3(T), dim3(256), 0, st, mp);
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, true>), dim3(T), dim3(256), 0, st, mp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, true>), dim3(T), dim3(256), 0, st, mp);
 }
 
 template <int DT, int FMT>
 void launch_k_up(const UpParams& up, bool gelu, hipStream_t st) {
   const int rows = FMT == SVDQ_FMT_MXFP4_G32 ? 128 : 64;
   const dim3 grid(unsigned(up.N / 128), unsigned(svdq::ceil_div(up.M, rows)));
-  if (gelu) hipLaunchKernelGGL((k_up<DT, FMT, true>), grid, dim3(256), 0, st, up);
-  else hipLaunchKernelGGL((k_up<DT, FMT, false>), grid, dim3(256), 0, st, up);
+  if (gelu) launch(SVDQ_KERNEL_OTHER, (k_up<DT, FMT, true>), grid, dim3(256), 0, st, up);
+  else launch(SVDQ_KERNEL_OTHER, (k_up<DT, FMT, false>), grid, dim3(256), 0, st, up);
 }
 
 svdq_status check_device_layer(const svdq_layer* L) {
@@ -2493,11 +2521,11 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
   if (i4) {
     const dim3 grid(unsigned(kp.N / 128), unsigned(w.Mp / 128));
     if (first->dtype == SVDQ_BF16) {
-      if (gelu) hipLaunchKernelGGL((k2_int4<SVDQ_BF16, true, true>), grid, dim3(256), 0, stream, kp);
-      else hipLaunchKernelGGL((k2_int4<SVDQ_BF16, false, true>), grid, dim3(256), 0, stream, kp);
+      if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_int4<SVDQ_BF16, true, true>), grid, dim3(256), 0, stream, kp);
+      else launch(SVDQ_KERNEL_GEMM, (k2_int4<SVDQ_BF16, false, true>), grid, dim3(256), 0, stream, kp);
     } else {
-      if (gelu) hipLaunchKernelGGL((k2_int4<SVDQ_F16, true, true>), grid, dim3(256), 0, stream, kp);
-      else hipLaunchKernelGGL((k2_int4<SVDQ_F16, false, true>), grid, dim3(256), 0, stream, kp);
+      if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_int4<SVDQ_F16, true, true>), grid, dim3(256), 0, stream, kp);
+      else launch(SVDQ_KERNEL_GEMM, (k2_int4<SVDQ_F16, false, true>), grid, dim3(256), 0, stream, kp);
     }
   } else {
     MxParams mp = mx_params(kp, w);
@@ -2523,11 +2551,11 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
     const int64_t n = w.Mp * tf.ncols4;
     const dim3 grid(unsigned((n + 63) / 64));
     if (i4) {
-      if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
-      else hipLaunchKernelGGL((k_tfin<SVDQ_F16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
+      if (first->dtype == SVDQ_BF16) launch(SVDQ_KERNEL_OTHER, (k_tfin<SVDQ_BF16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
+      else launch(SVDQ_KERNEL_OTHER, (k_tfin<SVDQ_F16, SVDQ_FMT_INT4_G64>), grid, dim3(256), 0, stream, tf);
     } else {
-      if (first->dtype == SVDQ_BF16) hipLaunchKernelGGL((k_tfin<SVDQ_BF16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
-      else hipLaunchKernelGGL((k_tfin<SVDQ_F16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
+      if (first->dtype == SVDQ_BF16) launch(SVDQ_KERNEL_OTHER, (k_tfin<SVDQ_BF16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
+      else launch(SVDQ_KERNEL_OTHER, (k_tfin<SVDQ_F16, SVDQ_FMT_MXFP4_G32>), grid, dim3(256), 0, stream, tf);
     }
   }
   return launch_ok();
@@ -2654,6 +2682,55 @@ extern "C" svdq_status svdq_trace_read(unsigned long long* records, int max_reco
   if (hipMemcpy(records, ptr, size_t(k) * 4 * sizeof(unsigned long long), hipMemcpyDeviceToHost) != hipSuccess)
     return SVDQ_ERR_HIP;
   return SVDQ_OK;
+}
+
+namespace {
+void timing_release(KernelTiming& t) {
+  for (hipEvent_t e : t.ev)
+    if (e) (void)hipEventDestroy(e);
+  t.ev.clear();
+  t.kind.clear();
+  t.used = 0;
+  t.on = false;
+}
+}  // namespace
+
+extern "C" svdq_status svdq_timing_start(int capacity) {
+  if (capacity < 1 || capacity > (1 << 20)) return SVDQ_ERR_INVALID_ARG;
+  KernelTiming& t = t_timing;
+  timing_release(t);
+  t.ev.assign(size_t(2) * size_t(capacity), nullptr);
+  t.kind.assign(size_t(capacity), 0);
+  for (hipEvent_t& e : t.ev) {
+    if (hipEventCreate(&e) != hipSuccess) {
+      e = nullptr;
+      timing_release(t);
+      return SVDQ_ERR_HIP;
+    }
+  }
+  t.on = true;
+  return SVDQ_OK;
+}
+
+extern "C" svdq_status svdq_timing_stop(int* kinds, float* ms, int max_launches, int* n_launches) {
+  if (!n_launches || max_launches < 0 || (max_launches > 0 && (!kinds || !ms))) return SVDQ_ERR_INVALID_ARG;
+  KernelTiming& t = t_timing;
+  t.on = false;
+  const size_t n = t.used;
+  *n_launches = int(n);
+  svdq_status st = SVDQ_OK;
+  for (size_t i = 0; i < n && i < size_t(max_launches); ++i) {
+    float v = 0.0f;
+    if (hipEventSynchronize(t.ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&v, t.ev[2 * i], t.ev[2 * i + 1]) != hipSuccess) {
+      st = SVDQ_ERR_HIP;
+      break;
+    }
+    kinds[i] = t.kind[i];
+    ms[i] = v;
+  }
+  timing_release(t);
+  return st;
 }
 
 extern "C" svdq_status svdq_activation_absmax(const void* X_dev, int64_t M, int64_t K, int64_t ldx,

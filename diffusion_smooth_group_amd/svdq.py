@@ -83,6 +83,8 @@ _SIGS = {
     "svdq_probe_clock": [_P, C.POINTER(C.c_double)],
     "svdq_trace_read": [_P, _I, C.POINTER(_I), C.POINTER(C.c_double)],
     "svdq_probe_mfma_rate": [_I, _I, _P, C.POINTER(C.c_double), C.POINTER(C.c_double)],
+    "svdq_timing_start": [_I],
+    "svdq_timing_stop": [C.POINTER(_I), C.POINTER(C.c_float), _I, C.POINTER(_I)],
 }
 
 _LIB = None
@@ -405,3 +407,24 @@ def activation_absmax(X, dtype: int, out=None, stream=None):
         out = torch.zeros(K, dtype=torch.float32, device=X.device)
     _call("svdq_activation_absmax", _t_ptr(X), M, K, X.stride(0), dtype, _t_ptr(out), _stream(stream))
     return out
+
+
+KERNEL_ACT, KERNEL_GEMM, KERNEL_OTHER = 1, 2, 3
+
+
+def timing_start(capacity: int):
+    """Time the calling thread's next `capacity` kernel launches from their
+    own dispatch timestamps (svdq_timing_stop returns them)."""
+    _call("svdq_timing_start", int(capacity))
+
+
+def timing_stop(max_launches: int = 1 << 16):
+    """Kinds (KERNEL_*) and durations in microseconds of the launches timed
+    since timing_start, in launch order."""
+    kinds = np.zeros(max_launches, dtype=np.int32)
+    ms = np.zeros(max_launches, dtype=np.float32)
+    n = C.c_int()
+    _call("svdq_timing_stop", kinds.ctypes.data_as(C.POINTER(C.c_int)), ms.ctypes.data_as(C.POINTER(C.c_float)),
+          int(max_launches), C.byref(n))
+    k = min(n.value, max_launches)
+    return kinds[:k].copy(), ms[:k].astype(np.float64) * 1e3

@@ -318,6 +318,33 @@ svdq_status svdq_probe_clock(hipStream_t stream, double* mhz);
  * mean shader clock over the loop.  1 <= iters <= 2^24.  Synchronous. */
 svdq_status svdq_probe_mfma_rate(int random_operands, int iters, hipStream_t stream, double* tflops, double* mhz);
 
+/* Kinds of kernel launch that svdq_timing_stop reports. */
+typedef enum {
+  SVDQ_KERNEL_ACT = 1,     /* activation kernel: smoothing, quantization, down-projection */
+  SVDQ_KERNEL_GEMM = 2,    /* the 4-bit (8-bit) GEMM with its fused epilogue */
+  SVDQ_KERNEL_OTHER = 3,   /* separate low-rank pass, chained T finalisation */
+  SVDQ_KERNEL_RANGE_MIN_ = -2147483647 - 1,   /* range markers, as for svdq_format */
+  SVDQ_KERNEL_RANGE_MAX_ = 2147483647
+} svdq_kernel_kind;
+
+/* Kernel durations taken from the kernels' own dispatch timestamps.
+ * svdq_timing_start(capacity): from this call on, the first `capacity`
+ * kernel launches that the calling host thread makes through this library
+ * (svdq_linear_forward, svdq_quantize_activations, svdq_gemm_forward, the
+ * chained forward; absmax and test hooks excepted) are made with
+ * hipExtLaunchKernel and an event pair of their own, which brackets that
+ * kernel alone -- nothing is inserted in the stream between kernels.
+ * Later launches run untimed.  1 <= capacity <= 2^20; the events are
+ * created here (the call allocates; a second start replaces the first).
+ * svdq_timing_stop(kinds, ms, max_launches, n_launches): ends recording,
+ * waits for the recorded kernels, and writes for the first
+ * min(*n_launches, max_launches) recorded launches, in launch order, their
+ * svdq_kernel_kind and duration in milliseconds; *n_launches = the number
+ * recorded.  Both act on the calling thread only; stop without start
+ * reports zero launches. */
+svdq_status svdq_timing_start(int capacity);
+svdq_status svdq_timing_stop(int* kinds, float* ms, int max_launches, int* n_launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,3 +55,34 @@ def test_probes_are_physical():
         assert 100.0 < mhz < 3000.0
         # dense FP4: 4096 flops per SIMD per clock, 1024 SIMDs
         assert 0.0 < tf <= 4096 * 1024 * mhz * 1e6 * 1e-12 * 1.02, (tf, mhz)
+
+
+@pytest.mark.parametrize("fmt", [o.MXFP4, o.INT4])
+def test_kernel_timing_records_each_launch(fmt):
+    # svdq_timing_start / stop: every kernel of the timed forwards is
+    # recorded in launch order with its kind, outputs stay bit-identical,
+    # and the kernels' durations fit inside the wall time of the loop
+    import torch
+    spec = wl.small_spec("timing", 600, 512, 768, o.BF16, fmt, 16, seed=(951, 0))
+    d = wl.generate(spec)
+    Xd = S.bits_to_device(d["X"], S.BF16, G.device())
+    lin = G.pack_gpu(d, fmt, 16, absmax=G.calib_absmax_gpu(Xd, o.BF16))
+    Y0 = lin.forward(Xd, gelu=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    S.timing_start(5)                   # room for two forwards and one more kernel
+    e0.record()
+    Ys = [lin.forward(Xd, gelu=True) for _ in range(3)]
+    e1.record()
+    torch.cuda.synchronize()
+    kinds, us = S.timing_stop()
+    assert list(kinds) == [S.KERNEL_ACT, S.KERNEL_GEMM] * 2 + [S.KERNEL_ACT]   # capacity 5: the rest untimed
+    assert np.all(us > 0.0)
+    assert us.sum() <= e0.elapsed_time(e1) * 1e3
+    for Y in Ys:
+        assert np.array_equal(S.device_to_bits(Y), S.device_to_bits(Y0))
+    # stopped: nothing more is recorded
+    lin.forward(Xd, gelu=True)
+    torch.cuda.synchronize()
+    kinds, us = S.timing_stop()
+    assert len(kinds) == 0

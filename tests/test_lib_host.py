@@ -107,6 +107,18 @@ def test_lora_capacity_and_forward_arg_errors():
     assert rc == 1
 
 
+def test_kernel_timing_argument_checks():
+    # no GPU call is made on these paths
+    lib = S.lib_handle()
+    assert lib.svdq_timing_start(0) == 1
+    assert lib.svdq_timing_start((1 << 20) + 1) == 1
+    n = C.c_int(-1)
+    assert lib.svdq_timing_stop(None, None, 0, C.byref(n)) == 0 and n.value == 0   # stop without start
+    assert lib.svdq_timing_stop(None, None, 1, C.byref(n)) == 1
+    assert lib.svdq_timing_stop(None, None, -1, C.byref(n)) == 1
+    assert lib.svdq_timing_stop(None, None, 0, None) == 1
+
+
 @pytest.mark.parametrize("dtype", [o.F16, o.BF16])
 @pytest.mark.parametrize("fmt", [o.INT4, o.MXFP4, o.INT8])
 @pytest.mark.parametrize("KN", [(256, 384), (640, 256)])
