@@ -670,37 +670,53 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One step = 8 rows (group g = 0, 1; weight tile i = 0..3), each row 4
+  // integer MFMAs (P) and 4 scale MFMAs (S) and then 16 convert + FMA pairs
+  // on the VALU.  The rows are software-pipelined: row r + 1's MFMAs are
+  // issued one by one between row r's dequant FMAs (P and S double-
+  // buffered), fenced so the compiler keeps that order, so the matrix core
+  // runs while the VALU dequantizes instead of each waiting on the other.
   auto compute = [&](const Ops& o) {
     // scale-MFMA operands: A row n holds (s_w[n][g0], s_w[n][g1]) at k = 0, 1;
     // B column m holds s_x[m][g] at k = g, so A B = s_w[n][g] s_x[m][g]
     f16x4 sa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa[i] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sw[i] : 0u, 0u});
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      i32x4 ub[4];
-      f16x4 sb[4];
+    i32x4 ub[4];
+    f16x4 sb[4];
+    auto token_side = [&](int g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
         sb[j] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sx[j] & (g ? 0xFFFF0000u : 0x0000FFFFu) : 0u, 0u});
       }
+    };
+    i32x4 P[2][4];
+    f32x4 S[2][4];
+    i32x4 ua;
+    auto mfma_pair = [&](int buf, int i, int j) {
+      P[buf][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
+      S[buf][j] = __builtin_amdgcn_mfma_f32_16x16x16f16(sa[i], sb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    };
+    token_side(0);
+    ua = widen_nibbles(o.a[0][0], o.a[0][1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const i32x4 ua = widen_nibbles(o.a[i][2 * g], o.a[i][2 * g + 1]);
-        // the row's integer MFMAs and scale products first, so each dequant
-        // finds its operands done
-        i32x4 P[4];
-        f32x4 S[4];
+    for (int j = 0; j < 4; ++j) mfma_pair(0, 0, j);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          P[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua, ub[j], i32x4{0, 0, 0, 0}, 0, 0, 0);
-          S[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(sa[i], sb[j], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        }
+    for (int r = 0; r < 8; ++r) {
+      const int c = r & 1, i = r & 3;
+      const int r1 = r + 1, g1 = r1 >> 2, i1 = r1 & 3;
+      if (r1 < 8) {
+        if (i1 == 0) token_side(g1);
+        ua = widen_nibbles(o.a[i1][2 * g1], o.a[i1][2 * g1 + 1]);
+      }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j) {
+        if (r1 < 8) mfma_pair(c ^ 1, i1, j);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(float(P[j][r]), S[j][r], acc[i][j][r]);
+        for (int q4 = 0; q4 < 4; ++q4) acc[i][j][q4] = __builtin_fmaf(float(P[c][j][q4]), S[c][j][q4], acc[i][j][q4]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };

@@ -278,10 +278,15 @@ svdq_status svdq_svd_factors(const void* W_host, int64_t K, int64_t N, int64_t l
                              float* lam);
 
 /* INT4 layers only: the per-group integer products P_g[m,n] = sum over the
- * 64 k of group g of code_x[m,k] code_w[k,n], as the GEMM's integer matrix
- * instructions produce them, for the window m in [m0, m0+nm), n in
- * [n0, n0+nn), g in [g0, g0+ng).  out_dev: int32 [ng][nm][nn] device
- * buffer.  Reads the codes svdq_quantize_activations left in ws_dev.
+ * 64 k of group g of code_x[m,k] code_w[k,n] for the window m in
+ * [m0, m0+nm), n in [n0, n0+nn), g in [g0, g0+ng).  A separate test kernel
+ * computes them; it is not the GEMM, but it forms each product the way the
+ * GEMM does -- the same nibble widening of the packed codes and the same
+ * 16 x 16 x 64 int8 matrix instruction on the same operand layout -- so
+ * the GEMM's partials equal these by construction (the GEMM feeds its own
+ * straight into the fp32 scale multiply-add and never stores them).
+ * out_dev: int32 [ng][nm][nn] device buffer.  Reads the codes
+ * svdq_quantize_activations left in ws_dev.
  * Requires m0 % 16 == 0, n0 % 16 == 0, nm % 16 == 0, nn % 16 == 0.
  * Asynchronous. */
 svdq_status svdq_int4_group_partials(const svdq_layer* layer, const void* ws_dev, size_t ws_bytes, int64_t M,
