@@ -83,6 +83,7 @@ def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, c
     torch.cuda.synchronize()
     Yb = S.device_to_bits(Y)
     ex = lin.export()
+    rows_sampled = rows is not None
     if rows is None:
         rows = np.arange(M)
     if cols is None:
@@ -104,4 +105,20 @@ def run_layer_case(d, fmt, rank, lora=False, gelu=False, rows=None, cols=None, c
             # T is rounded to 16 bits once from an fp32 (GPU) / fp64 (oracle) sum
             tol = np.abs(Tr).max() * (2.0 ** -7 if dt == o.BF16 else 2.0 ** -10) + 1e-30
             assert np.abs(Tg - Tr).max() <= tol, "down-projection T"
+        if rows_sampled:
+            # the activation pass is row-local and cheap to evaluate: codes,
+            # scales and T on many more rows than the output sample (every
+            # row where the oracle's quantizer is fast enough)
+            wide = np.arange(M) if (fmt != o.MXFP4 and M * K <= (1 << 26)) else \
+                np.union1d(rows, wl.random_rows(M, min(M, 1024), 97))
+            Xw = o.decode16(np.ascontiguousarray(d["X"][wide]), dt)
+            qa, sa, _ = o.quantize_activations(Xw, ex["invlam"], fmt)
+            assert np.array_equal(wx["codes"][wide].astype(np.int64), np.asarray(qa, np.int64)), \
+                f"activation codes ({len(wide)} rows)"
+            assert np.array_equal(wx["scales"][wide], sa), f"activation scales ({len(wide)} rows)"
+            Ta = o.decode16(o.down_projection(Xw, o.decode16(layer["L1x"], dt), dt), dt)
+            Tw = o.decode16(wx["T"][wide], dt)
+            if Ta.size:
+                tol = np.abs(Ta).max() * (2.0 ** -7 if dt == o.BF16 else 2.0 ** -10) + 1e-30
+                assert np.abs(Tw - Ta).max() <= tol, f"down-projection T ({len(wide)} rows)"
     return lin, {"fro": fro, "max": mx, "Y": Yb}
