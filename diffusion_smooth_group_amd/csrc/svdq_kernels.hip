@@ -1017,7 +1017,8 @@ struct MxParams {
   // columns; nx_l1x: its L1x in the activation kernel's tiling; nx_xq,
   // nx_sx: its workspace codes and scales (written here); nx_tp: fp32
   // partial down-projections [tiles_n][nx_Mp][nx_slots], one slab per
-  // 256-column tile of this layer (summed by k_tfin).
+  // column tile of this layer (256 columns in k2_mx, 192 in k2_mx8; summed
+  // by k_tfin).
   const float* nx_invlam;
   const uint16_t* nx_l1x;
   uint8_t* nx_xq;
@@ -1598,7 +1599,11 @@ static_assert(Pair::FR == 0 && Pair::SL == 1 && Pair::LPW == 8, "load classes");
 // weight / token tile in the workgroup tile (it fixes where each tile's e8m0
 // bytes sit in the pair dwords, byte 2 (tile % 2) + half); CLS: the wave's
 // load class (0: one more fragment half, one pair dword fewer).
-template <int DT, bool GELU, class C, int PA, int PB, int CLS>
+template <int DT, class C>
+__device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint8_t* smem, int wave, int lane,
+                                                   int64_t n0, int64_t m0);
+
+template <int DT, bool GELU, class C, int PA, int PB, int CLS, bool CHAIN = false>
 __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int wave, int lane, int64_t n0, int64_t m0) {
   constexpr int TI = C::TI, TJ = C::TJ, LPW = C::LPW;
   constexpr int NF = CLS == 0 ? C::FQ + 1 : C::FQ;                         // fragment slots
@@ -1911,12 +1916,118 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
   for (int pc = tid; pc < NPC; pc += 64 * C::NW) {
     const int row = pc / PPR, c = pc % PPR;
     const u32x4 val = *reinterpret_cast<const u32x4*>(smem + row * C::PITCH + c * 16);
-    if (m0 + row < p.M && n0 + 8 * c < p.N)
+    if (m0 + row < p.M && n0 + 8 * c < p.N && (!CHAIN || p.Y != nullptr))
       __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (m0 + row) * p.ldy + n0 + 8 * c));
+  }
+  if constexpr (CHAIN) mx8_chain_epilogue<DT, C>(p, smem, wave, lane, n0, m0);
+}
+
+// Epilogue chaining on the paired tiles: the staged TM x TN tile (rounded,
+// after GELU: the bits this layer would store) is the next layer's input
+// over columns n0 .. n0 + TN.  Codes and scales: unit (token tile t of 32
+// rows, 32-column block b) is one half-wave, lane = token row, applying the
+// activation kernel's MXFP4 rule and writing one 16-byte fragment piece and
+// one scale byte of the next layer's workspace (a 192-column tile covers
+// one and a half 128-deep steps of the next layer, so scale bytes, not
+// dwords, are stored).  Down-projection: each wave takes three 16-token
+// groups and, for every next-layer step the tile touches, runs the
+// 16 x 16 x 32 MFMAs with the step's L1x fragments, lanes whose k lies
+// outside the tile contributing zero, into this tile's fp32 partial slab.
+template <int DT, class C>
+__device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint8_t* smem, int wave, int lane,
+                                                   int64_t n0, int64_t m0) {
+  const int nst = int(p.N / KSTEP);                       // K steps of the next layer
+  const int64_t ntok32 = p.tiles_m_pad32;                 // 32-row token tiles in the next workspace
+  constexpr int TT = C::TM / 32, TB = C::TN / 32, NU = TT * TB;
+  const int half = lane >> 5, r32 = lane & 31;
+  for (int u0 = 2 * wave; u0 < NU; u0 += 2 * C::NW) {
+    const int u = u0 + half, t = u / TB, b = u % TB;
+    const int64_t col = n0 + 32 * b;
+    const int64_t tg = m0 / 32 + t;
+    if (u < NU && col < p.N && tg < ntok32) {
+      f32x4 il[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) il[e] = *reinterpret_cast<const f32x4*>(p.nx_invlam + col + 4 * e);
+      const uint8_t* src = smem + (32 * t + r32) * C::PITCH + 64 * b;
+      float xh[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + 16 * i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int x = 8 * i + 2 * e;
+          xh[x] = h2f<DT>(v[e] & 0xFFFFu) * il[x >> 2][x & 3];
+          xh[x + 1] = h2f<DT>(v[e] >> 16) * il[(x + 1) >> 2][(x + 1) & 3];
+        }
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int x = 0; x < 32; ++x) am = fmaxf(am, fabsf(xh[x]));
+      const int ex = e8m0_needs_slow(am) ? e8m0_slow(am) : e8m0_fast(am);
+      const float scl = ex != 0 ? __uint_as_float(unsigned(ex) << 23) : 1.0f;
+      unsigned d[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsigned v = 0u;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const unsigned cv = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, xh[8 * i + 2 * bb], xh[8 * i + 2 * bb + 1], scl, 0);
+          v |= (cv & 0xFFu) << (8 * bb);
+        }
+        d[i] = v;
+      }
+      const int s2 = int(col / KSTEP), bis = int((col % KSTEP) / 32);   // next-layer step, block in the step
+      *reinterpret_cast<u32x4*>(p.nx_xq + ((size_t(tg) * nst + s2) * 2 + (bis >> 1)) * 1024 + (r32 + 32 * (bis & 1)) * 16) =
+          u32x4{d[0], d[1], d[2], d[3]};
+      p.nx_sx[((size_t(tg >> 1) * nst + s2) * 64 + r32 + 32 * (bis & 1)) * 4 + 2 * (tg & 1) + (bis >> 1)] = uint8_t(ex);
+    }
+  }
+  if (p.nx_njt == 0) return;
+  // down-projection partials of this column tile
+  const int cs = p.nx_slots / 16;
+  const int q = lane >> 4;
+  const int64_t ncol = (n0 + C::TN < p.N ? n0 + C::TN : p.N);    // end of the tile's columns
+  const int s_first = int(n0 / KSTEP), s_last = int((ncol - 1) / KSTEP);
+  constexpr int NG = C::TM / 16;                                  // 16-token groups of the tile
+  constexpr int GPW = (NG + C::NW - 1) / C::NW;                   // per wave
+  const u32x4* l1x = reinterpret_cast<const u32x4*>(p.nx_l1x);
+  float* tp = p.nx_tp + (size_t(n0 / C::TN) * p.nx_Mp + m0) * p.nx_slots;
+  for (int jt = 0; jt < p.nx_njt; ++jt) {
+    f32x4 acc[GPW];
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s2 = s_first; s2 <= s_last; ++s2) {
+      u32x4 la[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) la[c] = l1x[((size_t(s2) * cs + jt) * 4 + c) * 64 + lane];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // MFMA c takes k in [32q + 8c, +8) of step s2 from lane group q
+        const int64_t k = int64_t(s2) * KSTEP + 32 * q + 8 * c;
+        const bool in = k >= n0 && k < ncol;
+        const int off = in ? int(k - n0) * 2 : 0;
+#pragma unroll
+        for (int g = 0; g < GPW; ++g) {
+          const int grp = wave + C::NW * g;
+          if (grp < NG) {
+            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (16 * grp + (lane & 15)) * C::PITCH + off);
+            acc[g] = mfma16<DT>(la[c], in ? v : u32x4{0u, 0u, 0u, 0u}, acc[g]);
+          }
+        }
+      }
+    }
+    // lane holds T[token 16 grp + lane % 16][16 jt + 4 q + i]
+#pragma unroll
+    for (int g = 0; g < GPW; ++g) {
+      const int grp = wave + C::NW * g;
+      const int64_t row = m0 + 16 * grp + (lane & 15);
+      if (grp < NG && row < p.nx_Mp)
+        *reinterpret_cast<f32x4*>(tp + size_t(16 * grp + (lane & 15)) * p.nx_slots + 16 * jt + 4 * q) = acc[g];
+    }
   }
 }
 
-template <int DT, bool GELU, class C>
+template <int DT, bool GELU, class C, bool CHAIN = false>
 __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
   trace_mark(p.trace, 0);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
@@ -1936,11 +2047,11 @@ __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
   // one load class (every wave issues the same stage loads), four tile parities
   static_assert(C::FR == 0, "one load class");
   if (pb == 0) {
-    if (pa == 0) mx8_tile<DT, GELU, C, 0, 0, 1>(p, smem, wave, lane, n0, m0);
-    else mx8_tile<DT, GELU, C, 1, 0, 1>(p, smem, wave, lane, n0, m0);
+    if (pa == 0) mx8_tile<DT, GELU, C, 0, 0, 1, CHAIN>(p, smem, wave, lane, n0, m0);
+    else mx8_tile<DT, GELU, C, 1, 0, 1, CHAIN>(p, smem, wave, lane, n0, m0);
   } else {
-    if (pa == 0) mx8_tile<DT, GELU, C, 0, 1, 1>(p, smem, wave, lane, n0, m0);
-    else mx8_tile<DT, GELU, C, 1, 1, 1>(p, smem, wave, lane, n0, m0);
+    if (pa == 0) mx8_tile<DT, GELU, C, 0, 1, 1, CHAIN>(p, smem, wave, lane, n0, m0);
+    else mx8_tile<DT, GELU, C, 1, 1, 1, CHAIN>(p, smem, wave, lane, n0, m0);
   }
   trace_mark(p.trace, 2);
 }
@@ -2269,6 +2380,18 @@ unsigned launch_k2_mx4(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, 
   return launch_k2_mx<DT>(kp, w, false, st);
 }
 
+// chained MXFP4 GEMM: with GELU the paired 192 x 192 tiles (as unchained),
+// else k2_mx; returns the partial-slab width (this layer's tile columns)
+template <int DT>
+int launch_k2_mx8_chain(MxParams mp, int64_t Mp, hipStream_t st) {
+  using C = mx8::Pair;
+  mp.tiles_n = int(svdq::ceil_div(mp.N, C::TN));
+  mp.tiles_m = int(svdq::ceil_div(Mp, C::TM));
+  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, true, C, true>), dim3(T), dim3(64 * C::NW), 0, st, mp);
+  return C::TN;
+}
+
 template <int DT>
 void launch_k2_mx_chain(const MxParams& mp, bool gelu, hipStream_t st) {
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
@@ -2483,8 +2606,10 @@ svdq_status check_chain(const svdq_layer* A, const svdq_layer* B) {
   return SVDQ_OK;
 }
 size_t chain_partials_offset(const svdq::WsOffsets& w) { return svdq::align256(w.total); }
-// output columns of `first` per partial slab: the GEMM's workgroup tile width
-int64_t chain_slab_cols(const svdq_layer* A) { return A->fmt == SVDQ_FMT_INT4_G64 ? 128 : 256; }
+// output columns of `first` per partial slab: the GEMM's workgroup tile
+// width (the workspace holds slabs for the narrowest, 192-column tiles of
+// the paired MXFP4 GEMM)
+int64_t chain_slab_cols(const svdq_layer* A) { return A->fmt == SVDQ_FMT_INT4_G64 ? 128 : 192; }
 size_t chain_partials_bytes(const svdq_layer* A, const svdq_layer* B, const svdq::WsOffsets& w) {
   return size_t(svdq::ceil_div(A->N, chain_slab_cols(A))) * size_t(w.Mp) * size_t(B->rank_slots) * 4;
 }
@@ -2534,6 +2659,7 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
   kp.nx_slots = next->rank_slots;
   // T column tiles of 16: INT4 fills whole 32-rank chunks (its T layout)
   kp.nx_njt = i4 ? 2 * int(svdq::ceil_div(next->rank_active, 32)) : int(svdq::ceil_div(next->rank_active, 16));
+  int64_t slab_cols = 128;
   if (i4) {
     const dim3 grid(unsigned(kp.N / 128), unsigned(w.Mp / 128));
     if (first->dtype == SVDQ_BF16) {
@@ -2553,8 +2679,14 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
     mp.nx_Mp = kp.nx_Mp;
     mp.nx_slots = kp.nx_slots;
     mp.nx_njt = kp.nx_njt;
-    if (first->dtype == SVDQ_BF16) launch_k2_mx_chain<SVDQ_BF16>(mp, gelu, stream);
-    else launch_k2_mx_chain<SVDQ_F16>(mp, gelu, stream);
+    if (gelu) {
+      slab_cols = first->dtype == SVDQ_BF16 ? launch_k2_mx8_chain<SVDQ_BF16>(mp, w.Mp, stream)
+                                            : launch_k2_mx8_chain<SVDQ_F16>(mp, w.Mp, stream);
+    } else {
+      if (first->dtype == SVDQ_BF16) launch_k2_mx_chain<SVDQ_BF16>(mp, false, stream);
+      else launch_k2_mx_chain<SVDQ_F16>(mp, false, stream);
+      slab_cols = 256;
+    }
   }
   if (kp.nx_njt > 0) {
     TfinParams tf;
@@ -2562,7 +2694,7 @@ extern "C" svdq_status svdq_linear_forward_chain(const svdq_layer* first, const 
     tf.t = reinterpret_cast<uint16_t*>(wsn + wn.t);
     tf.Mp = w.Mp;
     tf.slots = next->rank_slots;
-    tf.nparts = int(svdq::ceil_div(first->N, chain_slab_cols(first)));
+    tf.nparts = int(svdq::ceil_div(first->N, slab_cols));
     tf.ncols4 = 4 * kp.nx_njt;
     const int64_t n = w.Mp * tf.ncols4;
     const dim3 grid(unsigned((n + 63) / 64));
