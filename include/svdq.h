@@ -226,7 +226,8 @@ svdq_status svdq_gemm_forward(const svdq_layer* layer, int64_t M, void* Y_dev, i
  * epilogue and from the 16-bit output bits it would store, `next`'s
  * smoothing, group quantization (codes and scales into ws_next_dev) and
  * fp32 partial down-projections (one slab per GEMM column tile of `first`:
- * 256 output columns for MXFP4, 128 for INT4, in ws_dev); a small kernel
+ * 192 output columns for MXFP4 with GELU, 256 without, 128 for INT4; in
+ * ws_dev, sized by svdq_chain_workspace_size for the narrowest); a small kernel
  * then sums the slabs in a fixed order and rounds T once into ws_next_dev.
  * The activation pass of `next` over `first`'s output is gone;
  * svdq_gemm_forward(next, M, ..., ws_next_dev, ...) finishes `next`.  Codes
