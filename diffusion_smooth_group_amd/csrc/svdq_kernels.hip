@@ -1939,15 +1939,25 @@ __device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint
   const int nst = int(p.N / KSTEP);                       // K steps of the next layer
   const int64_t ntok32 = p.tiles_m_pad32;                 // 32-row token tiles in the next workspace
   constexpr int TT = C::TM / 32, TB = C::TN / 32, NU = TT * TB;
+  constexpr int NIT = (NU + 2 * C::NW - 1) / (2 * C::NW); // unit rounds per wave
   const int half = lane >> 5, r32 = lane & 31;
-  for (int u0 = 2 * wave; u0 < NU; u0 += 2 * C::NW) {
-    const int u = u0 + half, t = u / TB, b = u % TB;
+  // a unit's 1/lambda (32 columns) is requested one unit ahead
+  f32x4 il[2][8];
+  auto load_il = [&](int u, f32x4 (&dst)[8]) {
+    int64_t col = n0 + 32 * (u % TB);
+    col = (u < NU && col < p.N) ? col : 0;                // padding units read column 0 and store nothing
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[e] = *reinterpret_cast<const f32x4*>(p.nx_invlam + col + 4 * e);
+  };
+  load_il(2 * wave + half, il[0]);
+#pragma unroll
+  for (int k = 0; k < NIT; ++k) {
+    const int u = 2 * wave + 2 * C::NW * k + half, t = u / TB, b = u % TB;
+    if (k + 1 < NIT) load_il(u + 2 * C::NW, il[(k + 1) & 1]);
     const int64_t col = n0 + 32 * b;
     const int64_t tg = m0 / 32 + t;
     if (u < NU && col < p.N && tg < ntok32) {
-      f32x4 il[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) il[e] = *reinterpret_cast<const f32x4*>(p.nx_invlam + col + 4 * e);
+      const f32x4 (&ilk)[8] = il[k & 1];
       const uint8_t* src = smem + (32 * t + r32) * C::PITCH + 64 * b;
       float xh[32];
 #pragma unroll
@@ -1956,8 +1966,8 @@ __device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int x = 8 * i + 2 * e;
-          xh[x] = h2f<DT>(v[e] & 0xFFFFu) * il[x >> 2][x & 3];
-          xh[x + 1] = h2f<DT>(v[e] >> 16) * il[(x + 1) >> 2][(x + 1) & 3];
+          xh[x] = h2f<DT>(v[e] & 0xFFFFu) * ilk[x >> 2][x & 3];
+          xh[x + 1] = h2f<DT>(v[e] >> 16) * ilk[(x + 1) >> 2][(x + 1) & 3];
         }
       }
       float am = 0.0f;
@@ -1983,46 +1993,73 @@ __device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint
     }
   }
   if (p.nx_njt == 0) return;
-  // down-projection partials of this column tile
+  // down-projection partials of this column tile: the tile's staged values
+  // are read once (two next-layer steps x four MFMA k slices x the wave's
+  // 16-token groups) and reused for every 16-rank chunk; the L1x fragments
+  // of chunk jt + 1 are requested while chunk jt's MFMAs run
   const int cs = p.nx_slots / 16;
   const int q = lane >> 4;
   const int64_t ncol = (n0 + C::TN < p.N ? n0 + C::TN : p.N);    // end of the tile's columns
-  const int s_first = int(n0 / KSTEP), s_last = int((ncol - 1) / KSTEP);
+  const int s_first = int(n0 / KSTEP);
+  // next-layer steps a tile can touch (tiles start at multiples of 64 columns)
+  constexpr int NS = (C::TN + 64 + KSTEP - 1) / KSTEP;
+  static_assert(C::TN % 64 == 0, "tiles start at multiples of 64 columns");
   constexpr int NG = C::TM / 16;                                  // 16-token groups of the tile
   constexpr int GPW = (NG + C::NW - 1) / C::NW;                   // per wave
   const u32x4* l1x = reinterpret_cast<const u32x4*>(p.nx_l1x);
+  u32x4 xv[NS][4][GPW];
+#pragma unroll
+  for (int sv = 0; sv < NS; ++sv)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      // MFMA c takes k in [32q + 8c, +8) of step s_first + sv from lane group q
+      const int64_t k = int64_t(s_first + sv) * KSTEP + 32 * q + 8 * c;
+      const bool in = k >= n0 && k < ncol;
+      const int off = in ? int(k - n0) * 2 : 0;
+#pragma unroll
+      for (int g = 0; g < GPW; ++g) {
+        const int grp = wave + C::NW * g;
+        const u32x4 v = grp < NG ? *reinterpret_cast<const u32x4*>(smem + (16 * grp + (lane & 15)) * C::PITCH + off)
+                                 : u32x4{0u, 0u, 0u, 0u};
+        xv[sv][c][g] = in ? v : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  const int s_max = nst - 1;
+  u32x4 la[2][NS][4];
+  auto load_la = [&](int jt, u32x4 (&dst)[NS][4]) {
+#pragma unroll
+    for (int sv = 0; sv < NS; ++sv) {
+      const int s2 = s_first + sv <= s_max ? s_first + sv : s_max;   // a step past the layer reads the last (its lanes are zero)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[sv][c] = l1x[((size_t(s2) * cs + jt) * 4 + c) * 64 + lane];
+    }
+  };
   float* tp = p.nx_tp + (size_t(n0 / C::TN) * p.nx_Mp + m0) * p.nx_slots;
-  for (int jt = 0; jt < p.nx_njt; ++jt) {
-    f32x4 acc[GPW];
+  load_la(0, la[0]);
+  for (int jt = 0; jt < p.nx_njt; jt += 2) {
 #pragma unroll
-    for (int g = 0; g < GPW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = s_first; s2 <= s_last; ++s2) {
-      u32x4 la[4];
+    for (int h = 0; h < 2; ++h) {
+      const int j = jt + h;
+      if (j < p.nx_njt) {
+        if (j + 1 < p.nx_njt) load_la(j + 1, la[h ^ 1]);
+        f32x4 acc[GPW];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) la[c] = l1x[((size_t(s2) * cs + jt) * 4 + c) * 64 + lane];
+        for (int g = 0; g < GPW; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // MFMA c takes k in [32q + 8c, +8) of step s2 from lane group q
-        const int64_t k = int64_t(s2) * KSTEP + 32 * q + 8 * c;
-        const bool in = k >= n0 && k < ncol;
-        const int off = in ? int(k - n0) * 2 : 0;
+        for (int sv = 0; sv < NS; ++sv)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int g = 0; g < GPW; ++g) acc[g] = mfma16<DT>(la[h][sv][c], xv[sv][c][g], acc[g]);
+        // lane holds T[token 16 grp + lane % 16][16 j + 4 q + i]
 #pragma unroll
         for (int g = 0; g < GPW; ++g) {
           const int grp = wave + C::NW * g;
-          if (grp < NG) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(smem + (16 * grp + (lane & 15)) * C::PITCH + off);
-            acc[g] = mfma16<DT>(la[c], in ? v : u32x4{0u, 0u, 0u, 0u}, acc[g]);
-          }
+          const int64_t row = m0 + 16 * grp + (lane & 15);
+          if (grp < NG && row < p.nx_Mp)
+            *reinterpret_cast<f32x4*>(tp + size_t(16 * grp + (lane & 15)) * p.nx_slots + 16 * j + 4 * q) = acc[g];
         }
       }
-    }
-    // lane holds T[token 16 grp + lane % 16][16 jt + 4 q + i]
-#pragma unroll
-    for (int g = 0; g < GPW; ++g) {
-      const int grp = wave + C::NW * g;
-      const int64_t row = m0 + 16 * grp + (lane & 15);
-      if (grp < NG && row < p.nx_Mp)
-        *reinterpret_cast<f32x4*>(tp + size_t(16 * grp + (lane & 15)) * p.nx_slots + 16 * jt + 4 * q) = acc[g];
     }
   }
 }
