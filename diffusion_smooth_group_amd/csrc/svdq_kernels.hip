@@ -152,7 +152,7 @@ __device__ __forceinline__ void int4_quant_step(const float (&xh)[4][8], const f
     // it lies within 2^-18 of a half-integer; such lanes redo the group
     // with the correctly rounded division.
     const float inv = s32 != 0.0f ? 1.0f / s32 : 0.0f;
-    bool near = false;
+    unsigned near = 0u;                 // bit 8 cc + e: element (cc, e) lies near a half-integer
     float r[2][8];
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
@@ -160,13 +160,16 @@ __device__ __forceinline__ void int4_quant_step(const float (&xh)[4][8], const f
       for (int e = 0; e < 8; ++e) {
         const float qv = xh[2 * g + cc][e] * inv;
         r[cc][e] = rintf(qv);
-        near |= fabsf(qv - r[cc][e]) >= 0.5f - 0x1p-18f;
+        near |= (fabsf(qv - r[cc][e]) >= 0.5f - 0x1p-18f ? 1u : 0u) << (8 * cc + e);
       }
-    if (__builtin_expect(near, 0)) {
+    if (__builtin_expect(near != 0u, 0)) {
+      // only the near elements take the division (each one under a branch
+      // the wave skips when no lane needs it)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r[cc][e] = s32 != 0.0f ? rintf(xh[2 * g + cc][e] / s32) : 0.0f;
+        for (int e = 0; e < 8; ++e)
+          if (near & (1u << (8 * cc + e))) r[cc][e] = s32 != 0.0f ? rintf(xh[2 * g + cc][e] / s32) : 0.0f;
     }
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
