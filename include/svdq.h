@@ -347,7 +347,8 @@ typedef enum {
  * min(*n_launches, max_launches) recorded launches, in launch order, their
  * svdq_kernel_kind and duration in milliseconds; *n_launches = the number
  * recorded.  Both act on the calling thread only; stop without start
- * reports zero launches. */
+ * reports zero launches.  The events belong to the device current at
+ * svdq_timing_start: time launches on that device only. */
 svdq_status svdq_timing_start(int capacity);
 svdq_status svdq_timing_stop(int* kinds, float* ms, int max_launches, int* n_launches);
 
