@@ -1492,42 +1492,49 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     SVDQ_WAIT_VM(0);
 
     // ---- epilogue: (GELU,) round; stage the wave's 128 x 128 tile in LDS as
-    // [token][column] rows, then store whole 256-byte row segments
+    // [token][column] rows, then store whole 256-byte row segments.  The
+    // tile goes in two halves of 64 tokens: the second half's GELU and
+    // staging run while the first half's stores drain.  Both halves stay
+    // staged, so the chained epilogue below sees the whole tile.
     SVDQ_WAIT_LGKM0();
     __builtin_amdgcn_s_barrier();          // every wave is done with the LDS ring
     uint8_t* ob = smem + wave * (128 * mx::OUT_PITCH);
     const int64_t nw = n0 + 128 * wn;      // first column of this wave's tile
+    const int64_t mw = m0 + 128 * wm;      // first token of this wave's tile
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        // accumulator 4gg + r of tile (i, j): column 32i + 8gg + 4(lane / 32) + r, token 32j + lane % 32
-        const int nl = 32 * i + 8 * gg + 4 * (lane >> 5);
+      for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float vv[4];
+        for (int gg = 0; gg < 4; ++gg) {
+          // accumulator 4gg + r of tile (i, j): column 32i + 8gg + 4(lane / 32) + r, token 32j + lane % 32
+          const int nl = 32 * i + 8 * gg + 4 * (lane >> 5);
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            vv[x] = acc[i][j][4 * gg + x];
-            if constexpr (GELU) vv[x] = gelu_erf(vv[x]);
+          for (int jj = 0; jj < 2; ++jj) {
+            const int j = 2 * hf + jj;
+            float vv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              vv[x] = acc[i][j][4 * gg + x];
+              if constexpr (GELU) vv[x] = gelu_erf(vv[x]);
+            }
+            const int ml = 32 * j + (lane & 31);
+            *reinterpret_cast<u32x2*>(ob + ml * mx::OUT_PITCH + nl * 2) = u32x2{pack2<DT>(vv[0], vv[1]), pack2<DT>(vv[2], vv[3])};
           }
-          const int ml = 32 * j + (lane & 31);
-          *reinterpret_cast<u32x2*>(ob + ml * mx::OUT_PITCH + nl * 2) = u32x2{pack2<DT>(vv[0], vv[1]), pack2<DT>(vv[2], vv[3])};
         }
       }
-    }
-    SVDQ_WAIT_LGKM0();
-    const int64_t mw = m0 + 128 * wm;      // first token of this wave's tile
-    if (nw < p.N && (!CHAIN || p.Y != nullptr)) {
-      // non-temporal stores: Y is not read again here, and streaming it out
-      // leaves fewer dirty lines for the next kernel's reads to wait behind
+      SVDQ_WAIT_LGKM0();
+      if (nw < p.N && (!CHAIN || p.Y != nullptr)) {
+        // non-temporal stores: Y is not read again here, and streaming it out
+        // leaves fewer dirty lines for the next kernel's reads to wait behind
 #pragma unroll 4
-      for (int it = 0; it < 32; ++it) {
-        const int row = 4 * it + (lane >> 4);
-        const int col = (lane & 15) * 8;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
-        if (mw + row < p.M)
-          __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col));
+        for (int it = 16 * hf; it < 16 * hf + 16; ++it) {
+          const int row = 4 * it + (lane >> 4);
+          const int col = (lane & 15) * 8;
+          const u32x4 val = *reinterpret_cast<const u32x4*>(ob + row * mx::OUT_PITCH + col * 2);
+          if (mw + row < p.M)
+            __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(p.Y + (mw + row) * p.ldy + nw + col));
+        }
       }
     }
     if constexpr (CHAIN) chain_epilogue<DT>(p, smem, ob, wave, lane, m0, n0, nw, mw);
