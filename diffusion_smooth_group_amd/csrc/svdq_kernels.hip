@@ -26,6 +26,7 @@
 
 #include <cstdint>
 #include <mutex>
+#include <atomic>
 #include <vector>
 
 #include "svdq.h"
@@ -198,41 +199,53 @@ struct K1Params {
 
 // One workgroup = 16 tokens; its 4 waves take the 128-deep K steps round
 // robin, and lane l = m + 16q holds token m.  MXFP4: lane group q holds the
-// whole 32-block q of a step (four 16-byte loads of consecutive k), so the
+// whole 32-block q of a step (k in [32q + 8c, +8) for c = 0..3), so the
 // block maximum, exponent and codes are the lane's own work.  INT4: in
-// chunk c = 0..3 of a step the lane holds k in [32c + 8q, 32c + 8q + 8) (the
-// four lanes of a token read 64 contiguous bytes per load instruction), so
+// chunk c = 0..3 of a step the lane holds k in [32c + 8q, 32c + 8q + 8), so
 // a 64-group is chunks 2g and 2g + 1 of the token's four lanes.
+//
+// Loads.  MXFP4, and INT4 up to rank 32, read X row-contiguously: load c of
+// a step brings rows 4c .. 4c + 3 of the tile, 16 lanes per 256-byte row
+// segment, so every load instruction covers whole cache lines (the lane map
+// above touches 32 lines per instruction, a quarter of each, and streams X
+// markedly slower).  Each step then passes through the wave's own 4 KB LDS
+// buffer into the lane map: a lane stores its piece at its position in the
+// row and reads its own pieces back.  Lane (row r, position i) loads piece
+// i ^ r of the row, so a piece P of row m sits at position P ^ m and the
+// lane-map reads of 16 consecutive lanes fall in distinct banks.  INT4 with
+// wider ranks loads in the lane map itself: the extra offset registers would
+// spill beside its L1x fragments.
 //
 // Latency.  The vector memory counter retires in issue order, so waiting for
 // a short (L2) load also waits for every older HBM load.  Each step is
 // quantized and then projected (the down-projection MFMAs from the X still
 // in registers run on the matrix unit under the next step's quantization).
-// MXFP4 requests a chunk of steps' X at once (the HBM stream runs at full
-// rate while the light quantizer catches up); INT4, with more VALU work per
-// byte, keeps a rolling ring of steps in flight so its quantization
-// overlaps the stream.  Every memory operation is unconditional (indices
-// past the wave's last step are clamped, so padding steps rewrite
-// identical codes; their MFMAs are skipped), which keeps the compiler's
-// counter bookkeeping exact.  invlambda is copied to LDS (when it fits)
-// through registers.
+// A wave keeps a rolling ring of steps in flight (step i + R - 1's L1x and X
+// requested before step i is processed), so with one workgroup per compute
+// unit its quantization runs under its own stream.  When more than two
+// workgroups per compute unit queue up (CHUNK), MXFP4 instead requests
+// a whole chunk of steps' X at once: the resident workgroups' compute then
+// covers each other's waits, and the deeper request streams faster.  Every
+// memory operation is unconditional (indices past the wave's last step are
+// clamped, so padding steps rewrite identical codes; their MFMAs are
+// skipped), which keeps the compiler's counter bookkeeping exact.
+// invlambda is copied to LDS (when it fits) through registers.
 constexpr int K1_IL_LDS_MAX_K = 16384;
+constexpr int K1_XBUF_BYTES = 4 * 4096;    // the four waves' step buffers
 template <int NJT> struct K1Ring { static constexpr int value = NJT <= 2 ? 3 : (NJT <= 4 ? 2 : 1); };
 template <int NJT> struct K1Chunk { static constexpr int value = NJT <= 2 ? 6 : 2; };
 template <int NJT> struct K1LRing { static constexpr int value = NJT <= 4 ? 2 : 1; };
 
 // QUANT = false runs the down-projection alone (the unfused low-rank
 // baseline's separate pass over X): no codes, scales or invlambda.
-template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true>
+template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true, bool CHUNK = false>
 __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves per SIMD at least
-  // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction buffer
+  // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction
+  // buffer, then the waves' step buffers
   extern __shared__ __attribute__((aligned(16))) uint8_t k1_lds[];
-  // MXFP4 (little VALU work per byte) requests a whole chunk of steps at
-  // once; INT4 (more VALU work per byte) and ranks above 64 (whose L1x
-  // fragments fill the registers) keep a rolling ring in flight
-  constexpr bool MXC = FMT == SVDQ_FMT_MXFP4_G32 && NJT <= 4;
-  constexpr int R = MXC ? K1Chunk<NJT>::value : K1Ring<NJT>::value;   // X slots
-  constexpr int LR = MXC ? K1LRing<NJT>::value : R;                    // L1x slots
+  constexpr bool MXC = CHUNK && FMT == SVDQ_FMT_MXFP4_G32 && NJT <= 4;   // chunked requests
+  constexpr int R = MXC ? K1Chunk<NJT>::value : K1Ring<NJT>::value;   // X slots per wave
+  constexpr int LR = MXC ? K1LRing<NJT>::value : R;                    // L1x slots per wave
   const int mt = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
@@ -246,11 +259,27 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   // [32q + 8c, +8) for load c); INT4: a quarter of every block (k in
   // [32c + 8q, +8)), so a 64-group spans the four lanes of a token.
   constexpr bool MXL = FMT == SVDQ_FMT_MXFP4_G32;
-  constexpr int XC = MXL ? 8 : 32;               // element stride between a lane's loads
-  const uint16_t* xrow = p.X + row * p.ldx + (MXL ? 32 : 8) * q;
+  constexpr bool XT = MXL || NJT <= 2;           // row-contiguous loads through LDS
+  // XT: load c's row (4c + lane / 16) and the piece this lane loads,
+  // (lane % 16) ^ row, as element offsets from the tile's first row (a row
+  // past M reads row M - 1, which may lie before the tile).  Otherwise the
+  // lane-map row and its k offset.
+  const uint16_t* xtile = p.X + int64_t(mt) * 16 * p.ldx;
+  int xo[XT ? 4 : 1];
+  if constexpr (XT) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 4 * c + (lane >> 4);
+      xo[c] = int(min(int64_t(mt) * 16 + r, p.M - 1) - int64_t(mt) * 16) * int(p.ldx) + 8 * ((lane & 15) ^ r);
+    }
+  } else {
+    xo[0] = int(row - int64_t(mt) * 16) * int(p.ldx) + 8 * q;
+  }
   const float* il_lds = reinterpret_cast<const float*>(k1_lds);
   // invlambda is copied in whole 1 KB pieces, so its LDS copy spans K rounded up to 256
-  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + (IL_LDS ? size_t((p.K + 255) & ~int64_t(255)) * 4 : 0));   // [4][NJT][64]
+  const size_t il_span = IL_LDS ? size_t((p.K + 255) & ~int64_t(255)) * 4 : 0;
+  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + il_span);   // [4][NJT][64]
+  uint8_t* xb = k1_lds + il_span + size_t(4) * NJT * 64 * 16 + wave * 4096;   // this wave's step buffer
 
   // invlambda goes to LDS through registers and LDS stores, not direct
   // global->LDS loads: after those the compiler makes the first LDS read
@@ -300,8 +329,25 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   auto load_x = [&](int slot, int i) {
     const int s = step_of(i);
 #pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      if constexpr (XT) xr[slot][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[c] + s * KSTEP));
+      else xr[slot][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[0] + s * KSTEP + 32 * c));
+    }
+  };
+  // a landed step through the wave's LDS buffer into the lane map: row r at
+  // r * 256, each lane's piece at its own position; piece P of row m is read
+  // back from position P ^ m.  The wave's LDS operations run in order, so
+  // the next step's stores cannot overtake these reads.
+  auto to_lane_map = [&](int slot) {
+    if constexpr (!XT) return;
+#pragma unroll
     for (int c = 0; c < 4; ++c)
-      xr[slot][c] = *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + XC * c);
+      *reinterpret_cast<u32x4*>(xb + (4 * c + (lane >> 4)) * 256 + 16 * (lane & 15)) = xr[slot][c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int P = MXL ? 4 * q + c : 4 * c + q;
+      xr[slot][c] = *reinterpret_cast<const u32x4*>(xb + m * 256 + 16 * (P ^ m));
+    }
   };
   auto load_l1x = [&](int slot, int i) {
     const int s = step_of(i);
@@ -413,6 +459,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       }
 #pragma unroll
       for (int d = 0; d < R; ++d) {
+        to_lane_map(d);
         if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
         project(d, d % LR, i0 + d);
         if (d + LR < R) load_l1x(d % LR, i0 + d + LR);
@@ -444,6 +491,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
 #pragma unroll
       for (int d = 0; d < R; ++d) {
         load_step((d + R - 1) % R, i0 + d + R - 1);
+        to_lane_map(d);
         if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
         if constexpr (R == 1) load_l1x(d, i0 + d);
         project(d, d, i0 + d);
@@ -2327,32 +2375,58 @@ void launch(svdq_kernel_kind kind, F kernel, dim3 grid, dim3 block, unsigned lds
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-template <int FMT, int DT>
-void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
+// compute units of the current device (queried once per device)
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+template <int FMT, int DT, bool CHUNK>
+void launch_k1_as(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
   const bool il = kp.K <= K1_IL_LDS_MAX_K;
   const size_t il_bytes = il ? size_t((kp.K + 255) & ~int64_t(255)) * 4 : 0;
-  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
+  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16 + K1_XBUF_BYTES; };
   if (kp.njt == 0) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, true>), grid, block, il_bytes, st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, false>), grid, block, 0, st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, true, true, CHUNK>), grid, block, il_bytes + K1_XBUF_BYTES, st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, false, true, CHUNK>), grid, block, K1_XBUF_BYTES, st, kp);
   } else if (kp.njt <= 2) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, true>), grid, block, il_bytes + red_bytes(2), st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false>), grid, block, red_bytes(2), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, true, true, CHUNK>), grid, block, il_bytes + red_bytes(2), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false, true, CHUNK>), grid, block, red_bytes(2), st, kp);
   } else if (kp.njt <= 4) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, true>), grid, block, il_bytes + red_bytes(4), st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false>), grid, block, red_bytes(4), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, true, true, CHUNK>), grid, block, il_bytes + red_bytes(4), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false, true, CHUNK>), grid, block, red_bytes(4), st, kp);
   } else {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, true>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false>), grid, block, red_bytes(MAXJT), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, true, true, CHUNK>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false, true, CHUNK>), grid, block, red_bytes(MAXJT), st, kp);
   }
+}
+
+template <int FMT, int DT>
+void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
+  // MXFP4 requests whole chunks of steps once more than two workgroups per
+  // compute unit queue up
+  if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
+    if (Mp / 16 > 2 * int64_t(device_cus())) {
+      launch_k1_as<FMT, DT, true>(kp, Mp, st);
+      return;
+    }
+  }
+  launch_k1_as<FMT, DT, false>(kp, Mp, st);
 }
 
 // the down-projection alone (njt > 0)
 template <int FMT, int DT>
 void launch_k1_proj(const K1Params& kp, int64_t Mp, hipStream_t st) {
   const dim3 grid(unsigned(Mp / 16)), block(256);
-  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16; };
+  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16 + K1_XBUF_BYTES; };
   if (kp.njt <= 2) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false, false>), grid, block, red_bytes(2), st, kp);
   else if (kp.njt <= 4) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false, false>), grid, block, red_bytes(4), st, kp);
   else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false, false>), grid, block, red_bytes(MAXJT), st, kp);
