@@ -50,6 +50,18 @@ def test_mxfp4_more_tiles_than_cus_full_parity():
     G.run_layer_case(d, o.MXFP4, 16, lora=True, gelu=True)
 
 
+@pytest.mark.parametrize("rank,lora", [(0, 0), (32, 0), (32, 16)])
+@pytest.mark.parametrize("K", [640, 3072])
+def test_mxfp4_activation_many_workgroups_full_parity(K, rank, lora):
+    # 8300 tokens (528 activation workgroups of 16 on an 8448-row workspace):
+    # more than two per compute unit on a 256-CU device, where the MXFP4
+    # activation kernel requests whole chunks of steps; K = 640 gives waves
+    # one or two steps (padding steps in every chunk), K = 3072 six; rank 0,
+    # 32 and 48 cover the kernel's three chunk shapes; every output checked
+    d = _small(8300, K, 256, o.BF16, o.MXFP4, rank, lora=lora, seed=35)
+    G.run_layer_case(d, o.MXFP4, rank, lora=lora > 0)
+
+
 @pytest.mark.parametrize("dtype", [o.BF16, o.F16])
 def test_int4_many_tiles_full_parity(dtype):
     # 17 x 32 = 544 INT4 GEMM tiles of 128 x 128, more than two per compute
