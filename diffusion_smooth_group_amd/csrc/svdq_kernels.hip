@@ -1077,7 +1077,26 @@ struct MxParams {
   float* nx_tp;
   int64_t nx_Mp;
   int nx_slots, nx_njt;
+  // staggered start: the odd-indexed ones among the first stagger_wgs
+  // workgroups sleep stagger_sleeps x 8128 clocks before their first tile
+  int stagger_wgs, stagger_sleeps;
 };
+
+// Staggered start.  Workgroups are dealt to the XCDs round robin, so the
+// odd-indexed workgroups of the first round are those of the odd XCDs.
+// Holding them back for a few microseconds keeps the two halves of the chip
+// out of phase for the rest of the launch: one half's epilogues and stores
+// fall inside the other half's K loops instead of every tile switching
+// between the matrix-core phase and the store phase at once, and the
+// power-limited clock runs higher.  FLUX fc1, MXFP4, one box, one process:
+// 0 / 1 / 2 / 3 / 4 sleeps of 8128 clocks give 101.7 / 96.7 / 94.6 / 95.9 /
+// 99.5 us, the tiles' clock 1.81 -> 2.06 GHz at 2; the delay itself is paid
+// once, so launches of fewer than three rounds gain nothing (FLUX QKV, 2.5
+// rounds: +1%).  Staggering half of every XCD instead is slower than none.
+__device__ __forceinline__ void stagger_start(int wgs, int sleeps) {
+  if (int(blockIdx.x) < wgs && (blockIdx.x & 1))
+    for (int i = 0; i < sleeps; ++i) __builtin_amdgcn_s_sleep(127);
+}
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x16 __attribute__((ext_vector_type(16)));
@@ -1219,6 +1238,7 @@ __device__ __forceinline__ void chain_epilogue(const MxParams& p, const uint8_t*
 template <int DT, bool GELU, bool CHAIN = false, bool I8 = false>
 __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   trace_mark(p.trace, 0);
+  stagger_start(p.stagger_wgs, p.stagger_sleeps);
   // one LDS object (a second one makes the compiler wait for every global->LDS
   // load before any LDS read)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
@@ -2125,6 +2145,7 @@ __device__ __forceinline__ void mx8_chain_epilogue(const MxParams& p, const uint
 template <int DT, bool GELU, class C, bool CHAIN = false>
 __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
   trace_mark(p.trace, 0);
+  stagger_start(p.stagger_wgs, p.stagger_sleeps);
   __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // XCD-aware grouped tile order (as in k2_mx)
@@ -2467,10 +2488,19 @@ MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   return mp;
 }
 
+// staggered start (stagger_start) for launches of more than three rounds
+constexpr int kStaggerSleeps = 2;
+void set_stagger(MxParams& mp, unsigned wgs, int per_cu) {
+  const int round = per_cu * device_cus();
+  mp.stagger_wgs = int64_t(wgs) > 3 * int64_t(round) ? round : 0;
+  mp.stagger_sleeps = kStaggerSleeps;
+}
+
 template <int DT, bool I8 = false>
 unsigned launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
-  const MxParams mp = mx_params(kp, w);
+  MxParams mp = mx_params(kp, w);
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
+  set_stagger(mp, T, 1);
   if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
   else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
   return T;
@@ -2482,6 +2512,7 @@ unsigned launch_k2_mx8(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, 
   mp.tiles_n = int(svdq::ceil_div(kp.N, C::TN));
   mp.tiles_m = int(svdq::ceil_div(w.Mp, C::TM));
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  set_stagger(mp, T, C::WG_PER_CU);
   if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, true, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
   else launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, false, C>), dim3(T), dim3(64 * C::NW), 0, st, mp);
   return T;
@@ -2509,13 +2540,15 @@ int launch_k2_mx8_chain(MxParams mp, int64_t Mp, hipStream_t st) {
   mp.tiles_n = int(svdq::ceil_div(mp.N, C::TN));
   mp.tiles_m = int(svdq::ceil_div(Mp, C::TM));
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  set_stagger(mp, T, C::WG_PER_CU);
   launch(SVDQ_KERNEL_GEMM, (k2_mx8<DT, true, C, true>), dim3(T), dim3(64 * C::NW), 0, st, mp);
   return C::TN;
 }
 
 template <int DT>
-void launch_k2_mx_chain(const MxParams& mp, bool gelu, hipStream_t st) {
+void launch_k2_mx_chain(MxParams mp, bool gelu, hipStream_t st) {
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
+  set_stagger(mp, T, 1);
   if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, true>), dim3(T), dim3(256), 0, st, mp);
   else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, true>), dim3(T), dim3(256), 0, st, mp);
 }
