@@ -856,24 +856,45 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 // Pass 2 streams the workgroup's X again (96 KB at K = 3072, mostly from L2)
 // and writes the codes; each lane's 8 codes of a chunk are 8 contiguous
 // bytes of the INT8 fragment the GEMM (k2_mx with I8) reads.  Both passes keep the next step's loads in
-// flight; rows past M repeat row M - 1.
+// flight; rows past M repeat row M - 1.  X is loaded row-contiguously and
+// passed through the wave's LDS buffer into the lane map, as in k1_act.
 template <int DT, int NJT>
 __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   __shared__ float smax[4][16];
   __shared__ f32x4 red[4][NJT > 0 ? NJT : 1][64];
+  __shared__ __attribute__((aligned(16))) uint8_t xbuf[4][4096];   // the waves' step buffers
   const int mt = blockIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   const int64_t row = min(int64_t(mt) * 16 + m, p.M - 1);
   const int nsteps = int(p.K / KSTEP);
   const int nmine = (nsteps - wave + 3) / 4;
-  const uint16_t* xrow = p.X + row * p.ldx + 8 * q;
+  (void)row;
+  // load c's row (4c + lane / 16) and the piece this lane loads, (lane % 16)
+  // ^ row, as element offsets from the tile's first row
+  const uint16_t* xtile = p.X + int64_t(mt) * 16 * p.ldx;
+  int xo[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int r = 4 * c + (lane >> 4);
+    xo[c] = int(min(int64_t(mt) * 16 + r, p.M - 1) - int64_t(mt) * 16) * int(p.ldx) + 8 * ((lane & 15) ^ r);
+  }
   const int njc = p.njt > 0 ? p.njt - 1 : 0;
   auto step_of = [&](int i) { return nmine > 0 ? wave + 4 * (i < nmine ? i : nmine - 1) : 0; };
   auto load_x = [&](u32x4 (&x)[4], int i) {
     const int s = step_of(i);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4*>(xrow + s * KSTEP + 32 * c);
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4*>(xtile + (xo[c] + s * KSTEP));
+  };
+  // a landed step through the wave's LDS buffer into the lane map (piece
+  // 4c + q of row m sits at position (4c + q) ^ m)
+  uint8_t* xb = xbuf[wave];
+  auto to_lane_map = [&](u32x4 (&x)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(xb + (4 * c + (lane >> 4)) * 256 + 16 * (lane & 15)) = x[c];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = *reinterpret_cast<const u32x4*>(xb + m * 256 + 16 * ((4 * c + q) ^ m));
   };
   auto load_l1x = [&](u32x4 (&l)[NJT > 0 ? NJT : 1][4], int i) {
     const int s = step_of(i);
@@ -916,17 +937,19 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
     }
   };
   if constexpr (NJT <= 4) {
-    u32x4 xa[4], xb[4];
+    u32x4 xa[4], xb2[4];
     u32x4 la[NJT > 0 ? NJT : 1][4], lb[NJT > 0 ? NJT : 1][4];
     load_l1x(la, 0);
     load_x(xa, 0);
     for (int i = 0; i < nmine; i += 2) {
       load_l1x(lb, i + 1);
-      load_x(xb, i + 1);
+      load_x(xb2, i + 1);
+      to_lane_map(xa);
       pass1_step(xa, la, i);
       load_l1x(la, i + 2);
       load_x(xa, i + 2);
-      pass1_step(xb, lb, i + 1);
+      to_lane_map(xb2);
+      pass1_step(xb2, lb, i + 1);
     }
   } else {
     // ranks above 64: the wide L1x is loaded once per step, after X
@@ -935,6 +958,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
     for (int i = 0; i < nmine; ++i) {
       load_x(xa, i);
       load_l1x(la, i);
+      to_lane_map(xa);
       pass1_step(xa, la, i);
     }
   }
@@ -999,13 +1023,15 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
     }
   };
   {
-    u32x4 xa[4], xb[4];
+    u32x4 xa[4], xb2[4];
     load_x(xa, 0);
     for (int i = 0; i < nmine; i += 2) {
-      load_x(xb, i + 1);
+      load_x(xb2, i + 1);
+      to_lane_map(xa);
       pass2_step(xa, i);
       load_x(xa, i + 2);
-      pass2_step(xb, i + 1);
+      to_lane_map(xb2);
+      pass2_step(xb2, i + 1);
     }
   }
 }
