@@ -1106,6 +1106,10 @@ struct MxParams {
   // staggered start: the odd-indexed ones among the first stagger_wgs
   // workgroups sleep stagger_sleeps x 8128 clocks before their first tile
   int stagger_wgs, stagger_sleeps;
+  // k2_mx: XCD x (the workgroups with index % 8 == x) takes tiles
+  // [xcd_start[x], xcd_start[x] + xcd_count[x]) of the grouped order; its
+  // workgroups past the count have no tile
+  int xcd_start[8], xcd_count[8];
 };
 
 // Staggered start.  Workgroups are dealt to the XCDs round robin, so the
@@ -1289,10 +1293,13 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   {
     // XCD-aware tile index: workgroups are dealt to the 8 XCDs round robin,
     // so give XCD x a contiguous range of the tile order (they share its L2)
-    const int T = p.tiles_n * p.tiles_m;
     const int bid = blockIdx.x;
-    const int xcd = bid & 7, kx = bid >> 3, per = T >> 3, rem = T & 7;
-    const int tile = xcd * per + (xcd < rem ? xcd : rem) + kx;
+    const int xcd = bid & 7, kx = bid >> 3;
+    if (kx >= p.xcd_count[xcd]) {          // no tile (uniform over the workgroup)
+      trace_mark(p.trace, 2);
+      return;
+    }
+    const int tile = p.xcd_start[xcd] + kx;
     // grouped tile order: GROUP_M m-tiles sweep the n-tiles
     const int gsz_full = mx::GROUP_M * p.tiles_n;
     const int grp = tile / gsz_full, first_m = grp * mx::GROUP_M;
@@ -2498,6 +2505,35 @@ unsigned launch_k2_int4(const K2Params& kp, int64_t Mp, bool gelu, hipStream_t s
   return grid.x * grid.y;
 }
 
+// Tiles per XCD for k2_mx (T tiles, `slots` workgroups resident per XCD).
+// Evenly by default; with the staggered start (odd XCDs begin later), the
+// odd XCDs take whole rounds one fewer than the even ones need, so their
+// late start ends no later than the even XCDs' last round, as long as the
+// even XCDs then need no more rounds than an even split would.  Returns the
+// workgroups to launch (8 x the largest count).
+unsigned set_xcd_split(MxParams& mp, unsigned T, int slots) {
+  unsigned cnt[8];
+  for (int x = 0; x < 8; ++x) cnt[x] = T / 8 + (unsigned(x) < T % 8 ? 1u : 0u);
+  if (slots > 0) {
+    const unsigned rounds = (cnt[0] + unsigned(slots) - 1) / unsigned(slots);   // of the even split
+    const unsigned odd = (rounds - 1) * unsigned(slots);
+    if (rounds >= 2 && T > 4 * odd) {
+      const unsigned rest = T - 4 * odd;   // over the four even XCDs
+      if ((rest + 3) / 4 <= rounds * unsigned(slots)) {
+        for (int x = 0; x < 8; ++x) cnt[x] = (x & 1) ? odd : rest / 4 + (unsigned(x >> 1) < rest % 4 ? 1u : 0u);
+      }
+    }
+  }
+  unsigned start = 0, mx = 0;
+  for (int x = 0; x < 8; ++x) {
+    mp.xcd_start[x] = int(start);
+    mp.xcd_count[x] = int(cnt[x]);
+    start += cnt[x];
+    mx = cnt[x] > mx ? cnt[x] : mx;
+  }
+  return 8 * mx;
+}
+
 MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   MxParams mp = {};
   mp.wq = kp.wq; mp.sw = kp.sw; mp.l2 = kp.l2; mp.bias = kp.bias; mp.xq = kp.xq; mp.sx = kp.sx; mp.t = kp.t;
@@ -2511,6 +2547,7 @@ MxParams mx_params(const K2Params& kp, const svdq::WsOffsets& w) {
   mp.off_sx = int(kp.sx - kp.xq);
   mp.off_t = int(reinterpret_cast<const uint8_t*>(kp.t) - kp.xq);
   mp.trace = kp.trace;
+  set_xcd_split(mp, unsigned(mp.tiles_n) * unsigned(mp.tiles_m), 0);
   return mp;
 }
 
@@ -2525,11 +2562,12 @@ void set_stagger(MxParams& mp, unsigned wgs, int per_cu) {
 template <int DT, bool I8 = false>
 unsigned launch_k2_mx(const K2Params& kp, const svdq::WsOffsets& w, bool gelu, hipStream_t st) {
   MxParams mp = mx_params(kp, w);
-  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // one workgroup per 256 x 256 tile
+  const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);   // 256 x 256 tiles, one per workgroup
   set_stagger(mp, T, 1);
-  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, false, I8>), dim3(T), dim3(256), 0, st, mp);
-  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, false, I8>), dim3(T), dim3(256), 0, st, mp);
-  return T;
+  const unsigned G = mp.stagger_wgs > 0 ? set_xcd_split(mp, T, device_cus() / 8) : T;
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, false, I8>), dim3(G), dim3(256), 0, st, mp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, false, I8>), dim3(G), dim3(256), 0, st, mp);
+  return G;
 }
 
 template <int DT, class C>
@@ -2575,8 +2613,9 @@ template <int DT>
 void launch_k2_mx_chain(MxParams mp, bool gelu, hipStream_t st) {
   const unsigned T = unsigned(mp.tiles_n) * unsigned(mp.tiles_m);
   set_stagger(mp, T, 1);
-  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, true>), dim3(T), dim3(256), 0, st, mp);
-  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, true>), dim3(T), dim3(256), 0, st, mp);
+  const unsigned G = mp.stagger_wgs > 0 ? set_xcd_split(mp, T, device_cus() / 8) : T;
+  if (gelu) launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, true, true>), dim3(G), dim3(256), 0, st, mp);
+  else launch(SVDQ_KERNEL_GEMM, (k2_mx<DT, false, true>), dim3(G), dim3(256), 0, st, mp);
 }
 
 template <int DT, int FMT>

@@ -50,6 +50,15 @@ def test_mxfp4_more_tiles_than_cus_full_parity():
     G.run_layer_case(d, o.MXFP4, 16, lora=True, gelu=True)
 
 
+def test_mxfp4_staggered_uneven_split_full_parity():
+    # 17 x 48 = 816 tiles of 256 x 256, more than three rounds on 256 CUs:
+    # the launch staggers the odd XCDs and gives them 96 tiles against the
+    # even XCDs' 108, with workgroups past an XCD's count running no tile;
+    # ragged tokens (4300 of 4352), LoRA, every output checked
+    d = _small(4300, 256, 12288, o.BF16, o.MXFP4, 16, lora=16, seed=36)
+    G.run_layer_case(d, o.MXFP4, 16, lora=True)
+
+
 @pytest.mark.parametrize("rank,lora", [(0, 0), (32, 0), (32, 16)])
 @pytest.mark.parametrize("K", [640, 3072])
 def test_mxfp4_activation_many_workgroups_full_parity(K, rank, lora):
