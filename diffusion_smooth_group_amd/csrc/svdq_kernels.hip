@@ -229,7 +229,10 @@ struct K1Params {
 // memory operation is unconditional (indices past the wave's last step are
 // clamped, so padding steps rewrite identical codes; their MFMAs are
 // skipped), which keeps the compiler's counter bookkeeping exact.
-// invlambda is copied to LDS (when it fits) through registers.
+// invlambda is copied to LDS (when it fits) through registers.  Codes,
+// scales and T leave with non-temporal stores: the GEMM that reads them runs
+// on every XCD and reads them from memory anyway, and lines that do not sit
+// dirty in this kernel's L2s need no write-back before the GEMM may start.
 constexpr int K1_IL_LDS_MAX_K = 16384;
 constexpr int K1_XBUF_BYTES = 4 * 4096;    // the four waves' step buffers
 template <int NJT> struct K1Ring { static constexpr int value = NJT <= 2 ? 3 : (NJT <= 4 ? 2 : 1); };
@@ -394,9 +397,9 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       unsigned sh[2];
       int4_quant_step(xh, am, d, sh);
       uint8_t* frag = p.xq + (size_t(mt) * nsteps + s) * svdq::FRAG_BYTES;
-      *reinterpret_cast<u32x4*>(frag + lane * 16) = u32x4{d[0], d[1], d[2], d[3]};
+      __builtin_nontemporal_store(u32x4{d[0], d[1], d[2], d[3]}, reinterpret_cast<u32x4*>(frag + lane * 16));
       if (q == 0)
-        reinterpret_cast<unsigned*>(p.sx)[(size_t(mt) * nsteps + s) * 16 + m] = sh[0] | (sh[1] << 16);
+        __builtin_nontemporal_store(sh[0] | (sh[1] << 16), reinterpret_cast<unsigned*>(p.sx) + (size_t(mt) * nsteps + s) * 16 + m);
     } else {
       // the lane's own block: maximum, e8m0 exponent, 32 codes
       float a = 0.0f;
@@ -426,10 +429,10 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       // 32-row fragment tile t32 = mt / 2; block q of the step -> half q / 2,
       // lane (row in the 32-tile) + 32 (q % 2): one whole 16-byte piece
       const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
-      *reinterpret_cast<u32x4*>(p.xq + ((size_t(t32) * nsteps + s) * 2 + (q >> 1)) * 1024 + (r32 + 32 * (q & 1)) * 16) =
-          u32x4{d[0], d[1], d[2], d[3]};
+      __builtin_nontemporal_store(u32x4{d[0], d[1], d[2], d[3]},
+          reinterpret_cast<u32x4*>(p.xq + ((size_t(t32) * nsteps + s) * 2 + (q >> 1)) * 1024 + (r32 + 32 * (q & 1)) * 16));
       // scale byte 2 (t32 % 2) + q / 2 of the dword of lane (row + 32 (q % 2))
-      p.sx[((size_t(t32 >> 1) * nsteps + s) * 64 + r32 + 32 * (q & 1)) * 4 + 2 * (t32 & 1) + (q >> 1)] = uint8_t(ex);
+      __builtin_nontemporal_store(uint8_t(ex), p.sx + ((size_t(t32 >> 1) * nsteps + s) * 64 + r32 + 32 * (q & 1)) * 4 + 2 * (t32 & 1) + (q >> 1));
     }
   };
 
@@ -522,7 +525,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
         const int ldst = m + 16 * (2 * (jt & 1) + (q >> 1));
         dst = p.t + ((size_t(mt) * (p.slots / 32) + (jt >> 1)) * 64 + ldst) * 8 + 4 * (q & 1);
       }
-      *reinterpret_cast<u32x2*>(dst) = u32x2{lo, hi};
+      __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2*>(dst));
     }
   }
 }
@@ -857,7 +860,8 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
 // and writes the codes; each lane's 8 codes of a chunk are 8 contiguous
 // bytes of the INT8 fragment the GEMM (k2_mx with I8) reads.  Both passes keep the next step's loads in
 // flight; rows past M repeat row M - 1.  X is loaded row-contiguously and
-// passed through the wave's LDS buffer into the lane map, as in k1_act.
+// passed through the wave's LDS buffer into the lane map, and the outputs
+// leave with non-temporal stores, as in k1_act.
 template <int DT, int NJT>
 __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   __shared__ float smax[4][16];
@@ -973,7 +977,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
   // below 2^-128 the reciprocal overflows: such a token takes the division
   // for every code
   const bool inv_inf = !(inv <= 3.40282347e38f);
-  if (wave == 0 && q == 0) reinterpret_cast<float*>(p.sx)[size_t(mt) * 16 + m] = sc;
+  if (wave == 0 && q == 0) __builtin_nontemporal_store(sc, reinterpret_cast<float*>(p.sx) + size_t(mt) * 16 + m);
   if constexpr (NJT > 0) {
     // T = the four waves' partial sums (fixed order), rounded once, in the
     // GEMM's low-rank layout (32-row tiles, 16-rank chunks); lane holds
@@ -984,7 +988,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
       for (int w = 1; w < 4; ++w) v += red[w][jt][lane];
       const int t32 = mt >> 1, r32 = 16 * (mt & 1) + m;
       uint16_t* dst = p.t + ((size_t(t32) * (p.slots / 16) + jt) * 64 + r32 + 32 * (q >> 1)) * 8 + 4 * (q & 1);
-      *reinterpret_cast<u32x2*>(dst) = u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])};
+      __builtin_nontemporal_store(u32x2{pack2<DT>(v[0], v[1]), pack2<DT>(v[2], v[3])}, reinterpret_cast<u32x2*>(dst));
     }
   }
   // pass 2: codes rint(x_hat / s), from x_hat * (1/s) except for lanes whose
@@ -1019,7 +1023,7 @@ __global__ __launch_bounds__(256, 2) void k1_w8(K1Params p) {
       // k = 128 s + 32 c + 8 q + e: 64-deep step 2s + c/2, half c % 2, lane
       // (row in the 32-row tile) + 32 (q / 2), byte 8 (q % 2) + e
       const size_t frag = ((size_t(t32) * nst64 + 2 * s + (c >> 1)) * 2 + (c & 1)) * 64 + r32 + 32 * (q >> 1);
-      *reinterpret_cast<u32x2*>(p.xq + frag * 16 + 8 * (q & 1)) = u32x2{d[0], d[1]};
+      __builtin_nontemporal_store(u32x2{d[0], d[1]}, reinterpret_cast<u32x2*>(p.xq + frag * 16 + 8 * (q & 1)));
     }
   };
   {
