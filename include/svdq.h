@@ -301,8 +301,11 @@ svdq_status svdq_int4_group_partials(const svdq_layer* layer, const void* ws_dev
  * four counters -- wall clock and shader clock when the workgroup started,
  * wall clock and shader clock after its last store was issued.  The wall
  * clock runs at *wall_hz; cycles / wall time is the shader clock the
- * workgroup ran at.  Writes min(*n_records, max_records) records (4 x
- * uint64 each) to host memory `records`.  Synchronizes the device.  A
+ * workgroup ran at.  An MXFP4 or INT8 GEMM of more than three rounds of
+ * tiles launches workgroups past some XCDs' tile shares; those run no tile
+ * and record start and end a fraction of a microsecond apart.  Writes
+ * min(*n_records, max_records) records (4 x uint64 each) to host memory
+ * `records`.  Synchronizes the device.  A
  * library-owned array per device holds the trace: traced launches that
  * overlap on one device overwrite each other's records. */
 svdq_status svdq_trace_read(unsigned long long* records, int max_records, int* n_records, double* wall_hz);
