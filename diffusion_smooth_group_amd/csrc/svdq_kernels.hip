@@ -1461,39 +1461,44 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     };
     // Iteration r: wait until step r+1 is in LDS (its own loads, then the
     // barrier for everyone's), then run step r's 32 MFMAs with the reads of
-    // step r+1 and the refill of the stage step r-1 used (with step r+3)
-    // placed between them, fenced so the compiler keeps that order.
-    auto body_full = [&](int r, Frags& cur, Frags& nxt) {   // needs r + 3 < nk
+    // step r+1 and the refill of step r's own stage (with step r+4) placed
+    // between them, fenced so the compiler keeps that order.  Step r's
+    // fragments were read into registers during iteration r-1 and every
+    // wave retired those reads before this barrier, so its stage is free:
+    // all four stages hold steps in flight, and a step's loads get three
+    // iterations to land.
+    auto body_full = [&](int r, Frags& cur, Frags& nxt) {   // needs r + 4 < nk
       // cur's LDS reads were issued an iteration ago; retire them here so the
       // 20 reads below need no counter slot (lgkmcnt counts at most 15)
       SVDQ_WAIT_LGKM0();
-      SVDQ_WAIT_VM(LPS);
+      SVDQ_WAIT_VM(2 * LPS);                 // steps r+2 and r+3 may stay in flight
       __builtin_amdgcn_s_barrier();
       const uint8_t* rb = smem + ((r + 1) & 3) * mx::STAGE_BYTES;
-      uint8_t* lb = smem + ((r + 3) & 3) * mx::STAGE_BYTES;
+      uint8_t* lb = smem + (r & 3) * mx::STAGE_BYTES;
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
         mfma_k(cur, k);
-        mem_k(nxt, rb, lb, r + 3, k);
+        mem_k(nxt, rb, lb, r + 4, k);
         __builtin_amdgcn_sched_barrier(0);
       }
     };
-    // the last K steps: wait for step r+1 (if it is a K step), refill, read,
-    // compute step r
+    // the last K steps: wait for step r+1 (if it is a K step), refill step
+    // r's stage with step r+4, read step r+1, compute step r
     auto body_tail = [&](int r, Frags& cur, Frags& nxt) {
       SVDQ_WAIT_LGKM0();
       if (r + 1 < nk) {
-        if (r + 2 < total) SVDQ_WAIT_VM(LPS);
+        const int after = (r + 2 < total ? 1 : 0) + (r + 3 < total ? 1 : 0);   // steps requested after r+1
+        if (after == 2) SVDQ_WAIT_VM(2 * LPS);
+        else if (after == 1) SVDQ_WAIT_VM(LPS);
         else SVDQ_WAIT_VM(0);
         __builtin_amdgcn_s_barrier();
-        if (r + 3 < total) issue(r + 3, (r + 3) & 3);
+        if (r + 4 < total) issue(r + 4, r & 3);
         read_frags(nxt, (r + 1) & 3);
-      } else if (r + 3 < total) {
-        // the last K step still requests step r + 3 (the third low-rank
-        // step, when there are more than four 16-rank chunks): its stage
-        // held step r - 1, which every wave read before the previous
-        // step's barrier
-        issue(r + 3, (r + 3) & 3);
+      } else if (r + 4 < total) {
+        // the last K step still requests step r + 4 (a low-rank step):
+        // after this barrier every wave has retired its reads of step r
+        __builtin_amdgcn_s_barrier();
+        issue(r + 4, r & 3);
       }
       compute(cur);
     };
@@ -1510,9 +1515,10 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int r = 0; r < mx::STAGES - 1; ++r)
+    for (int r = 0; r < mx::STAGES; ++r)
       if (r < total) issue(r, r);
-    if (total > 2) SVDQ_WAIT_VM(2 * LPS);
+    if (total > 3) SVDQ_WAIT_VM(3 * LPS);
+    else if (total > 2) SVDQ_WAIT_VM(2 * LPS);
     else if (total > 1) SVDQ_WAIT_VM(LPS);
     else SVDQ_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
@@ -1547,7 +1553,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     Frags F0, F1;
     read_frags(F0, 0);
     int r = 0;
-    for (; r + 4 < nk; r += 2) {            // steady state: every step issued is a K step
+    for (; r + 5 < nk; r += 2) {            // steady state: every step issued is a K step
       body_full(r, F0, F1);
       body_full(r + 1, F1, F0);
     }
@@ -1582,15 +1588,18 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       }
       bias_mfma(true);
     }
-    // low-rank steps (their loads were issued during the last K steps)
+    // low-rank steps (up to four were issued during the last K steps)
     for (int q = nk; q < total; ++q) {
       SVDQ_WAIT_LGKM0();
       SVDQ_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();
-      if (q + 3 < total) issue(q + 3, (q + 3) & 3);
       Frags F;
       read_frags(F, q & 3);
       SVDQ_WAIT_LGKM0();
+      if (q + 4 < total) {
+        __builtin_amdgcn_s_barrier();      // every wave has read step q
+        issue(q + 4, q & 3);
+      }
       compute_lr(q - nk, F);
     }
     SVDQ_WAIT_LGKM0();

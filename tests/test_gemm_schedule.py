@@ -59,37 +59,41 @@ class Ring:
 
 
 def emulate_k2_mx(nk, nchunks16):
-    """k2_mx: 4-stage ring, prologue requests steps 0..2, step r + 3 is
-    requested while step r is computed (unit counts in load groups)."""
+    """k2_mx: 4-stage ring, the prologue requests steps 0..3, step r + 4 is
+    requested into step r's own stage while step r is computed (its
+    fragments were read into registers one iteration earlier); unit counts
+    in load groups."""
     total = nk + (nchunks16 + 1) // 2
     R = Ring(4, total)
-    for r in range(3):
+    for r in range(4):
         if r < total:
             R.issue(r)
-    R.wait_vm(2 if total > 2 else (1 if total > 1 else 0))
+    R.wait_vm(3 if total > 3 else (2 if total > 2 else (1 if total > 1 else 0)))
     R.barrier()
     R.read(0)
 
     def body_full(r):
+        assert r + 4 < nk
         R.wait_lgkm0()
-        R.wait_vm(1)
+        R.wait_vm(2)
         R.barrier()
         R.read(r + 1)
-        R.issue(r + 3)
+        R.issue(r + 4)
 
     def body_tail(r):
         R.wait_lgkm0()
         if r + 1 < nk:
-            R.wait_vm(1 if r + 2 < total else 0)
+            R.wait_vm(int(r + 2 < total) + int(r + 3 < total))
             R.barrier()
-            if r + 3 < total:
-                R.issue(r + 3)
+            if r + 4 < total:
+                R.issue(r + 4)
             R.read(r + 1)
-        elif r + 3 < total:
-            R.issue(r + 3)
+        elif r + 4 < total:
+            R.barrier()
+            R.issue(r + 4)
 
     r = 0
-    while r + 4 < nk:
+    while r + 5 < nk:
         body_full(r)
         body_full(r + 1)
         r += 2
@@ -102,10 +106,11 @@ def emulate_k2_mx(nk, nchunks16):
         R.wait_lgkm0()
         R.wait_vm(0)
         R.barrier()
-        if q + 3 < total:
-            R.issue(q + 3)
         R.read(q)
         R.wait_lgkm0()
+        if q + 4 < total:
+            R.barrier()
+            R.issue(q + 4)
     return R, total
 
 
@@ -195,18 +200,18 @@ def test_k2_mx8_stage_schedule(nk, stages):
 
 
 def test_emulation_catches_a_short_wait():
-    # the emulation itself must reject a schedule with one count too small:
-    # k2_mx waiting for vmcnt(2) groups in its steady step reads step r + 1
+    # the emulation itself must reject a schedule with one count too large:
+    # k2_mx waiting for vmcnt(3) groups in its steady step reads step r + 1
     # before it is complete
     total = 12
     R = Ring(4, total)
-    for r in range(3):
+    for r in range(4):
         R.issue(r)
-    R.wait_vm(2)
+    R.wait_vm(3)
     R.barrier()
     R.read(0)
     R.wait_lgkm0()
-    R.wait_vm(2)          # should be 1: it leaves steps 1 and 2 in flight
+    R.wait_vm(3)          # should be 2: it leaves steps 1, 2 and 3 in flight
     R.barrier()
     with pytest.raises(AssertionError):
         R.read(1)
@@ -221,3 +226,17 @@ def test_emulation_catches_an_early_refill():
     R.read(0)             # read issued, not waited for, no barrier since
     with pytest.raises(AssertionError):
         R.issue(4)        # stage 0 refilled while step 0 is still being read
+
+
+def test_emulation_catches_a_refill_without_barrier():
+    # k2_mx's last K step refills its own stage: without the barrier after
+    # every wave retired its reads of that step, the refill is rejected
+    R = Ring(4, 12)
+    for r in range(4):
+        R.issue(r)
+    R.wait_vm(0)
+    R.barrier()
+    R.read(0)
+    R.wait_lgkm0()        # this wave's reads retired, not yet published
+    with pytest.raises(AssertionError):
+        R.issue(4)
