@@ -1275,7 +1275,8 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
   stagger_start(p.stagger_wgs, p.stagger_sleeps);
   // one LDS object (a second one makes the compiler wait for every global->LDS
   // load before any LDS read)
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES];
+  // (the ring, then each wave's 128 bias values)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[mx::STAGES * mx::STAGE_BYTES + 4 * 512];
   // the wave index is uniform: keep it (and every LDS address derived from it) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int wn = wave & 1, wm = wave >> 1;
@@ -1504,16 +1505,21 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     };
     static_assert(mx::STAGES == 4, "the step bookkeeping assumes a 4-stage ring");
 
-    // The bias of this wave's 128 columns, issued before the stage loads so
-    // the prologue's wait covers it.  Lane l < 32 takes column 32i + l.
-    float bcol[4];
+    // The bias of this wave's 128 columns goes to LDS by the same buffer
+    // loads as the stages, issued before them so the prologue's wait for
+    // the first stage covers it.  (Loaded into registers, the compiler's
+    // wait before the first use would also wait for every stage issued
+    // after it.)  Lane l < 32 then takes column 32i + l.
+    float* bias_lds = reinterpret_cast<float*>(smem + mx::STAGES * mx::STAGE_BYTES + wave * 512);
+    {
+      const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc((void*)p.bias, 0, -1, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t nb = n0 + 128 * wn + 32 * i + (lane & 31);
-      nb = nb < p.N ? nb : p.N - 1;
-      bcol[i] = p.bias[nb];
+      for (int h = 0; h < 2; ++h) {
+        int64_t nb = n0 + 128 * wn + 64 * h + lane;
+        nb = nb < p.N ? nb : p.N - 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, (lds_ptr_t)(bias_lds + 64 * h), 4, int(nb) * 4, 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < mx::STAGES; ++r)
       if (r < total) issue(r, r);
@@ -1522,6 +1528,9 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     else if (total > 1) SVDQ_WAIT_VM(LPS);
     else SVDQ_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
+    float bcol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
     // Accumulators start at the bias: one 32 x 32 x 16 MFMA per tile with a
     // zero C operand (no separate zero fill or bias add).  A holds the
     // bias in k = 0..3 of lanes 0..31 (a 16-bit bias times 1.0 is exact), B of
@@ -1715,7 +1724,7 @@ struct Cfg {
 // with a GELU epilogue: one workgroup's epilogue runs under the other's K
 // loop); 384 x 192 and 256 x 256 eight-wave tiles were measured too
 using Pair = Cfg<2, 2, 3, 3, 3>;
-static_assert(Pair::LDS <= 80 * 1024, "two workgroups per compute unit");
+static_assert(Pair::LDS + Pair::NW * 512 <= 80 * 1024, "two workgroups per compute unit");
 static_assert(Pair::FR == 0 && Pair::SL == 1 && Pair::LPW == 8, "load classes");
 }  // namespace mx8
 
@@ -1853,15 +1862,19 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
                           2 * ((PB + j) & 1) + h);
   };
 
-  // ---- prologue: bias of this wave's columns, the first four stages
-  float bcol[TI];
+  // ---- prologue: bias of this wave's columns (to LDS by buffer loads, as
+  // in k2_mx, so only the first stage is waited for), the first stages
+  static_assert(TI * 32 <= 128, "a wave's bias values fit its 512 bytes");
+  float* bias_lds = reinterpret_cast<float*>(smem + C::LDS + wave * 512);
+  {
+    const __amdgpu_buffer_rsrc_t rbias = __builtin_amdgcn_make_buffer_rsrc((void*)p.bias, 0, -1, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < TI; ++i) {
-    int64_t nb_ = n0 + 32 * (ia0 + i) + (lane & 31);
-    nb_ = nb_ < p.N ? nb_ : p.N - 1;
-    bcol[i] = p.bias[nb_];
+    for (int h = 0; h < (TI * 32 + 63) / 64; ++h) {
+      int64_t nb_ = n0 + 32 * ia0 + 64 * h + lane;
+      nb_ = nb_ < p.N ? nb_ : p.N - 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rbias, (lds_ptr_t)(bias_lds + 64 * h), 4, int(nb_) * 4, 0, 0, 0);
+    }
   }
-  __builtin_amdgcn_sched_barrier(0);
   for (int r = 0; r < C::STAGES && r < total; ++r) {
 #pragma unroll
     for (int k = 0; k < LPW; ++k) issue_any(r, k);
@@ -1871,6 +1884,9 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
   else if (total > 1) SVDQ_WAIT_VM(LPW);
   else SVDQ_WAIT_VM(0);
   __builtin_amdgcn_s_barrier();
+  float bcol[TI];
+#pragma unroll
+  for (int i = 0; i < TI; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
   {
     // accumulators start at the bias (see k2_mx)
     const bool lo = lane < 32;
@@ -2192,7 +2208,8 @@ template <int DT, bool GELU, class C, bool CHAIN = false>
 __global__ __launch_bounds__(64 * C::NW, C::WG_PER_CU) void k2_mx8(MxParams p) {
   trace_mark(p.trace, 0);
   stagger_start(p.stagger_wgs, p.stagger_sleeps);
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+  // (the ring / output staging, then each wave's bias values)
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS + C::NW * 512];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // XCD-aware grouped tile order (as in k2_mx)
   const int T = p.tiles_n * p.tiles_m;
