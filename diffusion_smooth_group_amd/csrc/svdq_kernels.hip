@@ -1529,8 +1529,11 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
     else SVDQ_WAIT_VM(0);
     __builtin_amdgcn_s_barrier();
     float bcol[4];
+    auto read_bias = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
+      for (int i = 0; i < 4; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
+    };
+    if constexpr (!I8) read_bias();   // (I8 reads it after the K loop, so it is not live across it)
     // Accumulators start at the bias: one 32 x 32 x 16 MFMA per tile with a
     // zero C operand (no separate zero fill or bias add).  A holds the
     // bias in k = 0..3 of lanes 0..31 (a 16-bit bias times 1.0 is exact), B of
@@ -1595,6 +1598,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_convertvector(__builtin_bit_cast(i32x16, acc[i][j]), f32x16) * (swv * sxv[j]);
       }
+      read_bias();                           // the bias region of LDS is not part of the ring
       bias_mfma(true);
     }
     // low-rank steps (up to four were issued during the last K steps)
