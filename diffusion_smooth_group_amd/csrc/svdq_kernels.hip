@@ -241,21 +241,21 @@ template <int NJT> struct K1LRing { static constexpr int value = NJT <= 4 ? 2 : 
 
 // QUANT = false runs the down-projection alone (the unfused low-rank
 // baseline's separate pass over X): no codes, scales or invlambda.
-template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true, bool CHUNK = false>
-__global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves per SIMD at least
+template <int FMT, int DT, int NJT, bool IL_LDS, bool QUANT = true, bool CHUNK = false, int TT = 1>
+__global__ __launch_bounds__(256, TT == 1 ? 2 : 1) void k1_act(K1Params p) {   // TT = 1: two waves per SIMD at least
   // one LDS object: invlambda[0, K) (if IL_LDS), then the T reduction
   // buffer, then the waves' step buffers
   extern __shared__ __attribute__((aligned(16))) uint8_t k1_lds[];
   constexpr bool MXC = CHUNK && FMT == SVDQ_FMT_MXFP4_G32 && NJT <= 4;   // chunked requests
   constexpr int R = MXC ? K1Chunk<NJT>::value : K1Ring<NJT>::value;   // X slots per wave
   constexpr int LR = MXC ? K1LRing<NJT>::value : R;                    // L1x slots per wave
-  const int mt = blockIdx.x;
+  static_assert(TT == 1 || !MXC, "two-tile workgroups take the rolling ring");
+  const int mt0 = int(blockIdx.x) * TT;          // first 16-token tile of this workgroup
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int m = lane & 15, q = lane >> 4;
   // Rows past M (the workspace's padding up to its 256-row multiple) repeat
   // row M - 1: their codes, scales and T only ever meet GEMM outputs that are
   // not stored, and every load stays unconditional.
-  const int64_t row = min(int64_t(mt) * 16 + m, p.M - 1);
   const int nsteps = int(p.K / KSTEP);
   const int nmine = (nsteps - wave + 3) / 4;     // this wave's steps: wave, wave + 4, ...
   // MXFP4: lane group q holds the whole 32-block q of each step (k in
@@ -267,22 +267,26 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   // (lane % 16) ^ row, as element offsets from the tile's first row (a row
   // past M reads row M - 1, which may lie before the tile).  Otherwise the
   // lane-map row and its k offset.
-  const uint16_t* xtile = p.X + int64_t(mt) * 16 * p.ldx;
-  int xo[XT ? 4 : 1];
-  if constexpr (XT) {
+  // (the offsets of every tile of the workgroup count from its first tile's row)
+  const uint16_t* xtile = p.X + int64_t(mt0) * 16 * p.ldx;
+  int xo[TT][XT ? 4 : 1];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int r = 4 * c + (lane >> 4);
-      xo[c] = int(min(int64_t(mt) * 16 + r, p.M - 1) - int64_t(mt) * 16) * int(p.ldx) + 8 * ((lane & 15) ^ r);
+  for (int u = 0; u < TT; ++u) {
+    if constexpr (XT) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int r = 4 * c + (lane >> 4);
+        xo[u][c] = int(min(int64_t(mt0 + u) * 16 + r, p.M - 1) - int64_t(mt0) * 16) * int(p.ldx) + 8 * ((lane & 15) ^ r);
+      }
+    } else {
+      xo[u][0] = int(min(int64_t(mt0 + u) * 16 + m, p.M - 1) - int64_t(mt0) * 16) * int(p.ldx) + 8 * q;
     }
-  } else {
-    xo[0] = int(row - int64_t(mt) * 16) * int(p.ldx) + 8 * q;
   }
   const float* il_lds = reinterpret_cast<const float*>(k1_lds);
   // invlambda is copied in whole 1 KB pieces, so its LDS copy spans K rounded up to 256
   const size_t il_span = IL_LDS ? size_t((p.K + 255) & ~int64_t(255)) * 4 : 0;
-  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + il_span);   // [4][NJT][64]
-  uint8_t* xb = k1_lds + il_span + size_t(4) * NJT * 64 * 16 + wave * 4096;   // this wave's step buffer
+  f32x4* red = reinterpret_cast<f32x4*>(k1_lds + il_span);   // [4][TT][NJT][64]
+  uint8_t* xb = k1_lds + il_span + size_t(4) * TT * NJT * 64 * 16 + wave * 4096 * TT;   // this wave's step buffers
 
   // invlambda goes to LDS through registers and LDS stores, not direct
   // global->LDS loads: after those the compiler makes the first LDS read
@@ -319,23 +323,27 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     }
   }
 
-  f32x4 tacc[NJT > 0 ? NJT : 1];
+  f32x4 tacc[TT][NJT > 0 ? NJT : 1];
 #pragma unroll
-  for (int j = 0; j < NJT; ++j) tacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < TT; ++u)
+#pragma unroll
+    for (int j = 0; j < NJT; ++j) tacc[u][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int njc = p.njt > 0 ? p.njt - 1 : 0;
   // the step of ring index i: clamped to the wave's last step, and step 0
   // for a wave without steps (K < 512), whose ring prologue still loads
   auto step_of = [&](int i) { return nmine > 0 ? wave + 4 * (i < nmine ? i : nmine - 1) : 0; };
-  u32x4 xr[R][4];
+  u32x4 xr[R][TT][4];
   u32x4 lring[LR][NJT > 0 ? NJT : 1][4];
   auto load_x = [&](int slot, int i) {
     const int s = step_of(i);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if constexpr (XT) xr[slot][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[c] + s * KSTEP));
-      else xr[slot][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[0] + s * KSTEP + 32 * c));
-    }
+    for (int u = 0; u < TT; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if constexpr (XT) xr[slot][u][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[u][c] + s * KSTEP));
+        else xr[slot][u][c] = *reinterpret_cast<const u32x4*>(xtile + (xo[u][0] + s * KSTEP + 32 * c));
+      }
   };
   // a landed step through the wave's LDS buffer into the lane map: row r at
   // r * 256, each lane's piece at its own position; piece P of row m is read
@@ -344,13 +352,17 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
   auto to_lane_map = [&](int slot) {
     if constexpr (!XT) return;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      *reinterpret_cast<u32x4*>(xb + (4 * c + (lane >> 4)) * 256 + 16 * (lane & 15)) = xr[slot][c];
+    for (int u = 0; u < TT; ++u)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int P = MXL ? 4 * q + c : 4 * c + q;
-      xr[slot][c] = *reinterpret_cast<const u32x4*>(xb + m * 256 + 16 * (P ^ m));
-    }
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(xb + u * 4096 + (4 * c + (lane >> 4)) * 256 + 16 * (lane & 15)) = xr[slot][u][c];
+#pragma unroll
+    for (int u = 0; u < TT; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int P = MXL ? 4 * q + c : 4 * c + q;
+        xr[slot][u][c] = *reinterpret_cast<const u32x4*>(xb + u * 4096 + m * 256 + 16 * (P ^ m));
+      }
   };
   auto load_l1x = [&](int slot, int i) {
     const int s = step_of(i);
@@ -361,8 +373,8 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       for (int c = 0; c < 4; ++c) lring[slot][jt][c] = l1[((jt < njc ? jt : njc) * 4 + c) * 64];
   };
 
-  // quantize one step: codes and scales of 16 tokens x 128 k
-  auto quantize = [&](const u32x4 (&xq)[4], int s) {
+  // quantize one step: codes and scales of the 16 tokens of tile mt x 128 k
+  auto quantize = [&](const u32x4 (&xq)[4], int s, int mt) {
     // smoothed values x_hat = x * invlambda (one fp32 multiply)
     float xh[4][8];
 #pragma unroll
@@ -445,8 +457,14 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) tacc[jt] = mfma16<DT>(lring[lslot][jt][c], xr[slot][c], tacc[jt]);
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int u = 0; u < TT; ++u) tacc[u][jt] = mfma16<DT>(lring[lslot][jt][c], xr[slot][u][c], tacc[u][jt]);
     }
+  };
+  auto quantize_all = [&](int slot, int s) {
+#pragma unroll
+    for (int u = 0; u < TT; ++u) quantize(xr[slot][u], s, mt0 + u);
   };
   if constexpr (MXC) {
     // chunks of R steps: the L1x of the first LR steps, then all of the
@@ -463,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
 #pragma unroll
       for (int d = 0; d < R; ++d) {
         to_lane_map(d);
-        if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
+        if constexpr (QUANT) quantize_all(d, step_of(i0 + d));
         project(d, d % LR, i0 + d);
         if (d + LR < R) load_l1x(d % LR, i0 + d + LR);
       }
@@ -495,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
       for (int d = 0; d < R; ++d) {
         load_step((d + R - 1) % R, i0 + d + R - 1);
         to_lane_map(d);
-        if constexpr (QUANT) quantize(xr[d], step_of(i0 + d));
+        if constexpr (QUANT) quantize_all(d, step_of(i0 + d));
         if constexpr (R == 1) load_l1x(d, i0 + d);
         project(d, d, i0 + d);
       }
@@ -506,12 +524,15 @@ __global__ __launch_bounds__(256, 2) void k1_act(K1Params p) {   // two waves pe
     // T = the four waves' partial sums (fixed order), rounded once to 16 bits
     if (p.njt == 0) return;
 #pragma unroll
-    for (int jt = 0; jt < NJT; ++jt) red[(wave * NJT + jt) * 64 + lane] = tacc[jt];
-    __syncthreads();
-    for (int jt = wave; jt < p.njt; jt += 4) {
-      f32x4 v = red[jt * 64 + lane];
+    for (int u = 0; u < TT; ++u)
 #pragma unroll
-      for (int w = 1; w < 4; ++w) v += red[(w * NJT + jt) * 64 + lane];
+      for (int jt = 0; jt < NJT; ++jt) red[((wave * TT + u) * NJT + jt) * 64 + lane] = tacc[u][jt];
+    __syncthreads();
+    for (int ij = wave; ij < TT * p.njt; ij += 4) {
+      const int u = ij / p.njt, jt = ij - u * p.njt, mt = mt0 + u;
+      f32x4 v = red[(u * NJT + jt) * 64 + lane];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) v += red[((w * TT + u) * NJT + jt) * 64 + lane];
       // lane holds T[m][16 jt + 4q + i]; place it in the epilogue's B-fragment order
       const unsigned lo = pack2<DT>(v[0], v[1]);
       const unsigned hi = pack2<DT>(v[2], v[3]);
@@ -2476,22 +2497,22 @@ int device_cus() {
   return v;
 }
 
-template <int FMT, int DT, bool CHUNK>
+template <int FMT, int DT, bool CHUNK, int TT = 1>
 void launch_k1_as(const K1Params& kp, int64_t Mp, hipStream_t st) {
-  const dim3 grid(unsigned(Mp / 16)), block(256);
+  const dim3 grid(unsigned(Mp / (16 * TT))), block(256);
   const bool il = kp.K <= K1_IL_LDS_MAX_K;
   const size_t il_bytes = il ? size_t((kp.K + 255) & ~int64_t(255)) * 4 : 0;
-  auto red_bytes = [](int njt) { return size_t(4) * size_t(njt) * 64 * 16 + K1_XBUF_BYTES; };
+  auto red_bytes = [](int njt) { return size_t(TT) * (size_t(4) * size_t(njt) * 64 * 16 + K1_XBUF_BYTES); };
   if (kp.njt == 0) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, true, true, CHUNK>), grid, block, il_bytes + K1_XBUF_BYTES, st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, false, true, CHUNK>), grid, block, K1_XBUF_BYTES, st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, true, true, CHUNK, TT>), grid, block, il_bytes + red_bytes(0), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 0, false, true, CHUNK, TT>), grid, block, red_bytes(0), st, kp);
   } else if (kp.njt <= 2) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, true, true, CHUNK>), grid, block, il_bytes + red_bytes(2), st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false, true, CHUNK>), grid, block, red_bytes(2), st, kp);
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, true, true, CHUNK, TT>), grid, block, il_bytes + red_bytes(2), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 2, false, true, CHUNK, TT>), grid, block, red_bytes(2), st, kp);
   } else if (kp.njt <= 4) {
-    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, true, true, CHUNK>), grid, block, il_bytes + red_bytes(4), st, kp);
-    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false, true, CHUNK>), grid, block, red_bytes(4), st, kp);
-  } else {
+    if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, true, true, CHUNK, TT>), grid, block, il_bytes + red_bytes(4), st, kp);
+    else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, 4, false, true, CHUNK, TT>), grid, block, red_bytes(4), st, kp);
+  } else if constexpr (TT == 1) {   // (ranks above 64 keep one tile per workgroup)
     if (il) launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, true, true, CHUNK>), grid, block, il_bytes + red_bytes(MAXJT), st, kp);
     else launch(SVDQ_KERNEL_ACT, (k1_act<FMT, DT, MAXJT, false, true, CHUNK>), grid, block, red_bytes(MAXJT), st, kp);
   }
@@ -2499,11 +2520,24 @@ void launch_k1_as(const K1Params& kp, int64_t Mp, hipStream_t st) {
 
 template <int FMT, int DT>
 void launch_k1(const K1Params& kp, int64_t Mp, hipStream_t st) {
-  // MXFP4 requests whole chunks of steps once more than two workgroups per
-  // compute unit queue up
+  const int64_t tiles = Mp / 16, cus = int64_t(device_cus());
   if constexpr (FMT == SVDQ_FMT_MXFP4_G32) {
-    if (Mp / 16 > 2 * int64_t(device_cus())) {
+    // MXFP4 requests whole chunks of steps once more than two workgroups
+    // per compute unit queue up
+    if (tiles > 2 * cus) {
       launch_k1_as<FMT, DT, true>(kp, Mp, st);
+      return;
+    }
+    // More 16-token tiles than compute units and a long K: two tiles per
+    // workgroup, so each step's L1x fragments (twice the step's X bytes at
+    // rank 32, read from L2) serve 32 tokens; one workgroup reading L1x
+    // once for two tiles beats two workgroups on one compute unit reading
+    // it twice (FLUX fc2, K = 12288: 55.5 -> 49.0 us).  At K = 3072 the two
+    // forms take the same time.  INT4 keeps one tile per workgroup: its
+    // heavier quantizer would run at one wave per SIMD instead of two
+    // (62.0 -> 65.5 us at fc2).
+    if (tiles > cus && kp.njt <= 4 && kp.K >= 8192) {
+      launch_k1_as<FMT, DT, false, 2>(kp, Mp, st);
       return;
     }
   }

@@ -72,6 +72,18 @@ def test_mxfp4_activation_many_workgroups_full_parity(K, rank, lora):
 
 
 @pytest.mark.parametrize("dtype", [o.BF16, o.F16])
+@pytest.mark.parametrize("rank,lora", [(0, 0), (32, 0), (32, 16)])
+def test_activation_two_tile_workgroups_full_parity(dtype, rank, lora):
+    # 4300 tokens = 272 16-token tiles on a 4352-row workspace and K = 8192:
+    # more tiles than compute units on a 256-CU device and a long K, so each
+    # MXFP4 activation workgroup takes two tiles (one L1x fragment load per
+    # step for 32 tokens); ragged last tile; rank 0, 32 and 48 (the two ring
+    # depths); every code, scale, T row and output checked
+    d = _small(4300, 8192, 128, dtype, o.MXFP4, rank, lora=lora, seed=37)
+    G.run_layer_case(d, o.MXFP4, rank, lora=lora > 0)
+
+
+@pytest.mark.parametrize("dtype", [o.BF16, o.F16])
 def test_int4_many_tiles_full_parity(dtype):
     # 17 x 32 = 544 INT4 GEMM tiles of 128 x 128, more than two per compute
     # unit; ragged tokens (2100 of a 2304-row workspace), GELU, LoRA, every
