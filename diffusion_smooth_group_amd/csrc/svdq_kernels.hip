@@ -1544,17 +1544,11 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
 #pragma unroll
     for (int r = 0; r < mx::STAGES; ++r)
       if (r < total) issue(r, r);
-    if (total > 3) SVDQ_WAIT_VM(3 * LPS);
-    else if (total > 2) SVDQ_WAIT_VM(2 * LPS);
-    else if (total > 1) SVDQ_WAIT_VM(LPS);
-    else SVDQ_WAIT_VM(0);
-    __builtin_amdgcn_s_barrier();
     float bcol[4];
     auto read_bias = [&]() {
 #pragma unroll
       for (int i = 0; i < 4; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
     };
-    if constexpr (!I8) read_bias();   // (I8 reads it after the K loop, so it is not live across it)
     // Accumulators start at the bias: one 32 x 32 x 16 MFMA per tile with a
     // zero C operand (no separate zero fill or bias add).  A holds the
     // bias in k = 0..3 of lanes 0..31 (a 16-bit bias times 1.0 is exact), B of
@@ -1575,13 +1569,28 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         }
       }
     };
+    if constexpr (!I8) {
+      // This wave's bias region holds its own loads only, so no barrier:
+      // wait for the bias alone (every stage load was issued after it) and
+      // run the bias MFMAs while the first stage lands.  (I8 reads the bias
+      // after the K loop, so it is not live across it.)
+      if (total > 3) SVDQ_WAIT_VM(4 * LPS);
+      else if (total > 2) SVDQ_WAIT_VM(3 * LPS);
+      else if (total > 1) SVDQ_WAIT_VM(2 * LPS);
+      else SVDQ_WAIT_VM(LPS);
+      read_bias();
+      bias_mfma(false);
+    }
+    if (total > 3) SVDQ_WAIT_VM(3 * LPS);
+    else if (total > 2) SVDQ_WAIT_VM(2 * LPS);
+    else if (total > 1) SVDQ_WAIT_VM(LPS);
+    else SVDQ_WAIT_VM(0);
+    __builtin_amdgcn_s_barrier();
     if constexpr (I8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    } else {
-      bias_mfma(false);
     }
     Frags F0, F1;
     read_frags(F0, 0);
@@ -1904,11 +1913,13 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
 #pragma unroll
     for (int k = 0; k < LPW; ++k) issue_any(r, k);
   }
-  if (C::STAGES > 3 && total > 3) SVDQ_WAIT_VM(3 * LPW);
-  else if (total > 2) SVDQ_WAIT_VM(2 * LPW);
-  else if (total > 1) SVDQ_WAIT_VM(LPW);
-  else SVDQ_WAIT_VM(0);
-  __builtin_amdgcn_s_barrier();
+  // this wave's bias region holds its own loads only: wait for the bias
+  // alone (every stage load was issued after it), so the bias MFMAs run
+  // while the first stage lands
+  if (C::STAGES > 3 && total > 3) SVDQ_WAIT_VM(4 * LPW);
+  else if (total > 2) SVDQ_WAIT_VM(3 * LPW);
+  else if (total > 1) SVDQ_WAIT_VM(2 * LPW);
+  else SVDQ_WAIT_VM(LPW);
   float bcol[TI];
 #pragma unroll
   for (int i = 0; i < TI; ++i) bcol[i] = bias_lds[32 * i + (lane & 31)];
@@ -1928,6 +1939,11 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
       }
     }
   }
+  if (C::STAGES > 3 && total > 3) SVDQ_WAIT_VM(3 * LPW);
+  else if (total > 2) SVDQ_WAIT_VM(2 * LPW);
+  else if (total > 1) SVDQ_WAIT_VM(LPW);
+  else SVDQ_WAIT_VM(0);
+  __builtin_amdgcn_s_barrier();
 #pragma unroll
   for (int x = 0; x < NRD; ++x) rd_next(0, x);
 #pragma unroll
