@@ -1406,7 +1406,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
         issue_lr(r - nk, base);
       }
     };
-    auto read_frags = [&](Frags& F, int st) {
+    auto read_frags = [&](Frags& F, int st, bool scales = true) {   // (a low-rank step has no scales)
       const uint8_t* base = smem + st * mx::STAGE_BYTES;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -1418,7 +1418,7 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           F.a[i][h] = *reinterpret_cast<const u32x4*>(base + mx::A_OFF + ((4 * wn + i) * 2 + h) * 1024 + lane * 16);
-      if constexpr (!I8) {
+      if (!I8 && scales) {
         F.sb0 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm) * 256 + lane * 4);
         F.sb1 = *reinterpret_cast<const int*>(base + mx::SB_OFF + (2 * wm + 1) * 256 + lane * 4);
         F.sa0 = *reinterpret_cast<const int*>(base + mx::SA_OFF + (2 * wn) * 256 + lane * 4);
@@ -1637,12 +1637,14 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       SVDQ_WAIT_VM(0);
       __builtin_amdgcn_s_barrier();
       Frags F;
-      read_frags(F, q & 3);
-      SVDQ_WAIT_LGKM0();
+      read_frags(F, q & 3, false);
       if (q + 4 < total) {
+        SVDQ_WAIT_LGKM0();
         __builtin_amdgcn_s_barrier();      // every wave has read step q
         issue(q + 4, q & 3);
       }
+      // (otherwise the MFMAs wait for their own fragments only, so the
+      // first ones start while the later reads are still in flight)
       compute_lr(q - nk, F);
     }
     SVDQ_WAIT_LGKM0();
@@ -2047,8 +2049,8 @@ __device__ __forceinline__ void mx8_tile(const MxParams& p, uint8_t* smem, int w
 #pragma unroll
       for (int j = 0; j < TJ; ++j) fb[h][j] = rd_b(st, h, j);
     }
-    SVDQ_WAIT_LGKM0();
     if (q + AHEAD < total) {
+      SVDQ_WAIT_LGKM0();
       __builtin_amdgcn_s_barrier();      // every wave has read stage q before it is refilled
 #pragma unroll
       for (int k = 0; k < LPW; ++k) issue_any(q + AHEAD, k);

@@ -68,6 +68,7 @@ def emulate_k2_mx(nk, nchunks16):
     for r in range(4):
         if r < total:
             R.issue(r)
+    R.wait_vm(min(4, total))               # the bias (loaded before the stages) alone
     R.wait_vm(3 if total > 3 else (2 if total > 2 else (1 if total > 1 else 0)))
     R.barrier()
     R.read(0)
@@ -107,8 +108,8 @@ def emulate_k2_mx(nk, nchunks16):
         R.wait_vm(0)
         R.barrier()
         R.read(q)
-        R.wait_lgkm0()
         if q + 4 < total:
+            R.wait_lgkm0()
             R.barrier()
             R.issue(q + 4)
     return R, total
@@ -123,6 +124,7 @@ def emulate_k2_mx8(nk, nchunks16, stages):
     R = Ring(stages, total)
     for r in range(min(stages, total)):
         R.issue(r)
+    R.wait_vm(min(stages, total))          # the bias (loaded before the stages) alone
     if stages > 3 and total > 3:
         R.wait_vm(3)
     elif total > 2:
@@ -174,8 +176,8 @@ def emulate_k2_mx8(nk, nchunks16, stages):
             R.wait_vm(0)
             R.barrier()
         R.read(q)
-        R.wait_lgkm0()
         if q + stages < total:
+            R.wait_lgkm0()
             R.barrier()
             R.issue(q + stages)
     return R, total
