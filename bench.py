@@ -555,6 +555,16 @@ def main():
     t_k2 = kus[kinds == S.KERNEL_GEMM]
     if len(t_k1) != n_inst or len(t_k2) != n_inst:
         raise RuntimeError(f"kernel timing recorded {len(t_k1)} / {len(t_k2)} launches, expected {n_inst}")
+    # per-forward times: an event pair around each forward on the stream the
+    # kernels run on (distribution of the step the headline averages)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (ea, eb) in enumerate(evs):
+        ea.record(stream)
+        fwd(i)
+        eb.record(stream)
+    torch.cuda.synchronize()
+    t_step = np.array([ea.elapsed_time(eb) * 1e3 for ea, eb in evs])
     sclk_after = S.probe_clock(stream)      # a light kernel right after the loop
     # three more forwards with the GEMM traced (per-workgroup wall and
     # shader-clock counters): the clock the GEMM itself ran at
@@ -637,6 +647,8 @@ def main():
                         "algorithmic_bytes_per_launch": k1_bytes(M, K, args.rank, fmt_name)},
         "kernel_us": {"k1_act": stats(t_k1), "k2_gemm": stats(t_k2), "k1_plus_k2": stats(t_fw),
                       "launches": n_inst, "forward_loop_us_per_step": round(ms_step_kt * 1e3, 2)},
+        "forward_us": dict(stats(t_step), note="one event pair around each of `steps` forwards (distribution "
+                                               "of the step the headline averages; the pairs add a little)"),
         "sclk_mhz": {"idle_probe": round(sclk_idle, 1), "probe_after_forward_loop": round(sclk_after, 1),
                      "gemm_traced": round(tr["sclk_mhz"], 1)},
         "k2_trace": {"workgroups": tr["workgroups"], "span_us": round(tr["span_us"], 2),
