@@ -708,6 +708,10 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int q = lane >> 4;
   const bool k0 = lane < 16;             // lanes that carry k = 0..3 of a 16 x 16 x 16 operand
+  // the scale operands' lane masks as AND masks (one instruction per
+  // operand instead of a mask and a select): all bits on lanes 0..15, and
+  // the low / high fp16 half of the scale dword for group 0 / 1
+  const unsigned mk0 = k0 ? 0xFFFFFFFFu : 0u, mg0 = mk0 & 0x0000FFFFu, mg1 = mk0 & 0xFFFF0000u;
   const int wn = wave & 1, wm = wave >> 1;
   const int64_t n0 = int64_t(blockIdx.x) * 128 + wn * 64;
   const int64_t m0 = int64_t(blockIdx.y) * 128 + wm * 64;
@@ -756,14 +760,14 @@ __global__ __launch_bounds__(256, 2) void k2_int4(K2Params p) {
     // B column m holds s_x[m][g] at k = g, so A B = s_w[n][g] s_x[m][g]
     f16x4 sa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sw[i] : 0u, 0u});
+    for (int i = 0; i < 4; ++i) sa[i] = __builtin_bit_cast(f16x4, u32x2{o.sw[i] & mk0, 0u});
     i32x4 ub[4];
     f16x4 sb[4];
     auto token_side = [&](int g) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         ub[j] = widen_nibbles(o.b[j][2 * g], o.b[j][2 * g + 1]);
-        sb[j] = __builtin_bit_cast(f16x4, u32x2{k0 ? o.sx[j] & (g ? 0xFFFF0000u : 0x0000FFFFu) : 0u, 0u});
+        sb[j] = __builtin_bit_cast(f16x4, u32x2{o.sx[j] & (g ? mg1 : mg0), 0u});
       }
     };
     i32x4 P[2][4];
