@@ -462,10 +462,6 @@ __global__ __launch_bounds__(256, TT == 1 ? 2 : 1) void k1_act(K1Params p) {   /
           for (int u = 0; u < TT; ++u) tacc[u][jt] = mfma16<DT>(lring[lslot][jt][c], xr[slot][u][c], tacc[u][jt]);
     }
   };
-  auto quantize_all = [&](int slot, int s) {
-#pragma unroll
-    for (int u = 0; u < TT; ++u) quantize(xr[slot][u], s, mt0 + u);
-  };
   if constexpr (MXC) {
     // chunks of R steps: the L1x of the first LR steps, then all of the
     // chunk's X; the steps are taken as they land, L1x streamed LR ahead
@@ -481,7 +477,12 @@ __global__ __launch_bounds__(256, TT == 1 ? 2 : 1) void k1_act(K1Params p) {   /
 #pragma unroll
       for (int d = 0; d < R; ++d) {
         to_lane_map(d);
-        if constexpr (QUANT) quantize_all(d, step_of(i0 + d));
+        if constexpr (QUANT) {
+          // (each tile's ring slot named at the call: a slot index passed
+          // through another lambda cost the one-tile kernels registers)
+#pragma unroll
+          for (int u = 0; u < TT; ++u) quantize(xr[d][u], step_of(i0 + d), mt0 + u);
+        }
         project(d, d % LR, i0 + d);
         if (d + LR < R) load_l1x(d % LR, i0 + d + LR);
       }
@@ -513,7 +514,12 @@ __global__ __launch_bounds__(256, TT == 1 ? 2 : 1) void k1_act(K1Params p) {   /
       for (int d = 0; d < R; ++d) {
         load_step((d + R - 1) % R, i0 + d + R - 1);
         to_lane_map(d);
-        if constexpr (QUANT) quantize_all(d, step_of(i0 + d));
+        if constexpr (QUANT) {
+          // (each tile's ring slot named at the call: a slot index passed
+          // through another lambda cost the one-tile kernels registers)
+#pragma unroll
+          for (int u = 0; u < TT; ++u) quantize(xr[d][u], step_of(i0 + d), mt0 + u);
+        }
         if constexpr (R == 1) load_l1x(d, i0 + d);
         project(d, d, i0 + d);
       }
@@ -529,7 +535,7 @@ __global__ __launch_bounds__(256, TT == 1 ? 2 : 1) void k1_act(K1Params p) {   /
       for (int jt = 0; jt < NJT; ++jt) red[((wave * TT + u) * NJT + jt) * 64 + lane] = tacc[u][jt];
     __syncthreads();
     for (int ij = wave; ij < TT * p.njt; ij += 4) {
-      const int u = ij / p.njt, jt = ij - u * p.njt, mt = mt0 + u;
+      const int u = TT == 1 ? 0 : ij / p.njt, jt = TT == 1 ? ij : ij - u * p.njt, mt = mt0 + u;
       f32x4 v = red[(u * NJT + jt) * 64 + lane];
 #pragma unroll
       for (int w = 1; w < 4; ++w) v += red[((w * TT + u) * NJT + jt) * 64 + lane];
