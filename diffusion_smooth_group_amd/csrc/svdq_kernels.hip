@@ -197,7 +197,10 @@ struct K1Params {
   uint16_t* t;
 };
 
-// One workgroup = 16 tokens; its 4 waves take the 128-deep K steps round
+// One workgroup = 16 tokens (TT = 2: two 16-token tiles, each wave taking
+// its steps for both, so a step's L1x fragments -- the down-projection's A
+// operands, twice the step's X bytes at rank 32 -- are loaded once for 32
+// tokens; one wave per SIMD); its 4 waves take the 128-deep K steps round
 // robin, and lane l = m + 16q holds token m.  MXFP4: lane group q holds the
 // whole 32-block q of a step (k in [32q + 8c, +8) for c = 0..3), so the
 // block maximum, exponent and codes are the lane's own work.  INT4: in
