@@ -1698,8 +1698,10 @@ __global__ __launch_bounds__(256) void k2_mx(MxParams p) {
       SVDQ_WAIT_LGKM0();
       if (nw < p.N && (!CHAIN || p.Y != nullptr)) {
         // non-temporal stores: Y is not read again here, and streaming it out
-        // leaves fewer dirty lines for the next kernel's reads to wait behind
-#pragma unroll 4
+        // leaves fewer dirty lines for the next kernel's reads to wait behind;
+        // the half's 16 row reads all issued ahead of their stores (forward
+        // -1.4%, K2 -1.0% against four at a time, four interleaved rounds)
+#pragma unroll
         for (int it = 16 * hf; it < 16 * hf + 16; ++it) {
           const int row = 4 * it + (lane >> 4);
           const int col = (lane & 15) * 8;
