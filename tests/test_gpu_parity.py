@@ -83,6 +83,16 @@ def test_activation_two_tile_workgroups_full_parity(dtype, rank, lora):
     G.run_layer_case(d, o.MXFP4, rank, lora=lora > 0)
 
 
+@pytest.mark.parametrize("M", [4097, 8192])
+def test_activation_two_tile_workgroup_edges(M):
+    # the two-tile form at its edges: 4097 tokens (one real row in the last
+    # pair of tiles, the rest repeating it) and 8192 tokens (512 tiles, the
+    # largest count before the chunked one-tile form takes over on 256 CUs);
+    # K = 8192, rank 32, every code, scale, T row and output checked
+    d = _small(M, 8192, 128, o.BF16, o.MXFP4, 32, seed=38)
+    G.run_layer_case(d, o.MXFP4, 32)
+
+
 @pytest.mark.parametrize("dtype", [o.BF16, o.F16])
 def test_int4_many_tiles_full_parity(dtype):
     # 17 x 32 = 544 INT4 GEMM tiles of 128 x 128, more than two per compute
